@@ -1,0 +1,594 @@
+/*
+ * oracle.c -- plain, slow CPU reference for NVFP4 microscaled quantization
+ * (randomized Hadamard rotation, RTN, stochastic rounding, MS-EDEN), the IF4
+ * per-group FP4/INT4 selection, dequantization and the block-scaled FP4 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+ * CPU-baseline leg are its only users.  The product library never includes,
+ * links or calls it, and it shares no code with the GPU sources.
+ *
+ * Sources (the pages this follows), cited below by these short names:
+ *   [QII-abs]  Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved
+ *              Unbiased Gradient Estimation -- abstract (OpenAlex W7127094184).
+ *   [QII-sum]  Quartet II news summary (mind-verse.de), sections
+ *              "Kerninnovationen", "Quantisierung im Rueckwaertsdurchlauf",
+ *              "Quantisierung im Vorwaertsdurchlauf".
+ *   [PAL]      "Comparing INT4 and NVFP4 Palettes on Real Gradient Tensors"
+ *              (sethwheeler.dev): opening paragraph; section "The two corners,
+ *              and what the palette does to them".
+ *   [IF4]      Adaptive Block-Scaled Data Types / IF4 (arXiv 2603.28765, page
+ *              on thelatestinai.com): abstract, Figure 1, Table 1, Figure 3.
+ *   [Philox]   Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+ *              as 1, 2, 3", SC'11 -- the Philox-4x32 bijection (published
+ *              method; the pages do not fix a generator).
+ *
+ * Arithmetic: fp32 with one rounding per written operation (compiled with
+ * -ffp-contract=off), denormals kept.  Where the pages leave a step open the
+ * plainest reading is taken; each is marked READING.
+ *
+ * Parity pins (what each function is checked against, outside itself) are
+ * listed at each function.  Every function here is pinned.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ======================================================================
+ * Element and scale formats
+ * ==================================================================== */
+
+/* E2M1 magnitudes by 3-bit code: the sixteen values of the FP4 menu are
+ * {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6} [PAL opening paragraph].
+ * Code = sign<<3 | magnitude code.
+ * Pinned by: the grid fixture from [PAL]; gap ratio 4 from [PAL]. */
+static const float GRID_E2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+float orc_e2m1_value(int nibble) {
+  float m = GRID_E2M1[nibble & 7];
+  return (nibble & 8) ? -m : m;
+}
+
+/* E4M3 (OCP "FN" variant): sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, 0x7F/0xFF are NaN.  Largest finite 448 and smallest
+ * subnormal 2^-9 are what [IF4 Table 1] prints ("6 x 448", "0.5 x 2^-9").
+ * Pinned by: max 448, min 2^-9, 126 positive finite values. */
+float orc_e4m3_value(int byte) {
+  int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  float v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexpf((float)m, -9);               /* m/8 * 2^(1-7) */
+  else
+    v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+  return s ? -v : v;
+}
+
+/* The 127 non-negative finite E4M3 values, ascending, indexed by byte. */
+static float e4m3_pos(int byte) { return orc_e4m3_value(byte); }
+
+/* Largest j in [0, n-1) with grid(j) <= v (grid ascending, grid(0) <= v). */
+static int floor_index_e4m3(float v) {
+  int lo = 0, hi = 126; /* invariant: value(lo) <= v < value(hi) or hi==126 */
+  if (v >= e4m3_pos(126)) return 126;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (e4m3_pos(mid) <= v) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+/* READING (block-scale rounding for RTN and IF4): nearest E4M3 value, ties to
+ * the even mantissa, saturating at 448 (no infinities in E4M3 "FN"). */
+int orc_e4m3_rne_sat(float v) {
+  if (!(v > 0.0f)) return 0;
+  if (v >= 448.0f) return 0x7E;
+  int j = floor_index_e4m3(v);
+  float lo = e4m3_pos(j), hi = e4m3_pos(j + 1);
+  float dl = v - lo, dh = hi - v;
+  if (dl < dh) return j;
+  if (dh < dl) return j + 1;
+  return (j & 1) ? j + 1 : j;
+}
+
+/* READING (block-scale rounding for elementwise SR): round the scale UP, so
+ * that no element of the block lands above the top grid point -- the SR
+ * corner of [PAL] scales each block so that nothing clips.  Saturates at 448. */
+int orc_e4m3_ceil_sat(float v) {
+  if (!(v > 0.0f)) return 0;
+  if (v >= 448.0f) return 0x7E;
+  int j = floor_index_e4m3(v);
+  return (e4m3_pos(j) == v) ? j : j + 1;
+}
+
+/* READING (E2M1 round-to-nearest): nearest grid value, ties to the code with
+ * an even mantissa bit (0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4,
+ * 5->4).  Input is a magnitude already clipped to [0, 6]. */
+int orc_e2m1_rne(float a) {
+  int j = 0;
+  if (a >= 6.0f) return 7;
+  while (j < 7 && GRID_E2M1[j + 1] <= a) j++;
+  float dl = a - GRID_E2M1[j], dh = GRID_E2M1[j + 1] - a;
+  if (dl < dh) return j;
+  if (dh < dl) return j + 1;
+  return (j & 1) ? j + 1 : j;
+}
+
+/* Scaled-INT4 magnitudes 0..7 [IF4 Table 1, NVINT4 row: max 7, min 1].
+ * Round to nearest integer, ties to even; input clipped to [0, 7]. */
+int orc_int4_rne(float a) {
+  if (a >= 7.0f) return 7;
+  float f = floorf(a);
+  float frac = a - f;
+  int q = (int)f;
+  if (frac > 0.5f) q += 1;
+  else if (frac == 0.5f && (q & 1)) q += 1;
+  return q;
+}
+
+/* Stochastic rounding onto an ascending grid (elementwise SR of [QII-abs],
+ * [QII-sum]; unbiased: it rounds up with probability (a-l)/(u-l) [PAL]).
+ * READING (uniforms): a 16-bit uniform u; round up iff u < p * 65536, where
+ * p = (a - l)/(u - l).  Every grid gap here is a power of two, so p is exact.
+ * A value at the top of the grid keeps it.
+ * Pinned by: exact enumeration of all 65536 uniforms against the closed form
+ * E[(q - a)^2] = (a - l)(u - a) of [PAL]. */
+static int sr_on_grid(const float *grid, int n, float a, uint32_t u16) {
+  if (a >= grid[n - 1]) return n - 1;
+  int j = 0;
+  while (j < n - 1 && grid[j + 1] <= a) j++;
+  float lo = grid[j], hi = grid[j + 1];
+  float p = (a - lo) / (hi - lo);
+  return ((float)u16 < p * 65536.0f) ? j + 1 : j;
+}
+
+int orc_sr_e2m1(float a, uint32_t u16) { return sr_on_grid(GRID_E2M1, 8, a, u16); }
+
+int orc_sr_e4m3(float a, uint32_t u16) {
+  if (!(a > 0.0f)) return 0;
+  if (a >= 448.0f) return 0x7E;
+  int j = floor_index_e4m3(a);
+  float lo = e4m3_pos(j), hi = e4m3_pos(j + 1);
+  float p = (a - lo) / (hi - lo);
+  return ((float)u16 < p * 65536.0f) ? j + 1 : j;
+}
+
+/* ======================================================================
+ * Counter-based RNG: Philox-4x32 with 10 rounds [Philox].
+ * Each round multiplies words 0 and 2 by the two round multipliers, swaps
+ * in the high halves XORed with the other words and the round key; the key
+ * advances by the two Weyl increments between rounds.
+ * Pinned by: the published known-answer vectors.
+ * ==================================================================== */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; round++) {
+    if (round > 0) { k0 += W0; k1 += W1; }
+    uint64_t p0 = (uint64_t)M0 * (uint64_t)x0;
+    uint64_t p1 = (uint64_t)M1 * (uint64_t)x2;
+    uint32_t y0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    uint32_t y1 = (uint32_t)p1;
+    uint32_t y2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    uint32_t y3 = (uint32_t)p0;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* READING (RNG keying): key = seed (lo, hi words); counter = (idx>>3 lo,
+ * idx>>3 hi, tag, stream).  One Philox call yields eight 16-bit uniforms;
+ * uniform number (idx & 7) is half (idx & 1) of word (idx & 7) >> 1.
+ * tag 0 draws element roundings, tag 1 draws MS-EDEN scale roundings;
+ * idx is the element (tag 0) or block (tag 1) index in the output layout. */
+uint32_t orc_uniform16(uint64_t seed, uint32_t tag, uint32_t stream, uint64_t idx) {
+  uint64_t call = idx >> 3;
+  uint32_t ctr[4] = {(uint32_t)call, (uint32_t)(call >> 32), tag, stream};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  orc_philox4x32_10(ctr, key, w);
+  uint32_t word = w[(idx & 7) >> 1];
+  return (word >> (16 * (idx & 1))) & 0xFFFFu;
+}
+
+/* ======================================================================
+ * Randomized Hadamard rotation along the micro-scaling groups
+ * [QII-sum "Quantisierung im Rueckwaertsdurchlauf"; PAL opening paragraph].
+ * READING: 128-point Sylvester Hadamard in natural order, applied after a
+ * per-coordinate sign flip, normalized by fp32(1/sqrt(128)).  The fast
+ * transform runs stages of stride 1, 2, 4, ..., 64; each butterfly maps
+ * (a, b) -> (a + b, a - b) with a the lower index.
+ * Pinned by: H H^T = 128 I and H[i][j] = (-1)^popcount(i & j) (textbook
+ * Sylvester form), norm preservation, round trip, inner products of pairs
+ * rotated with the same signs.
+ * ==================================================================== */
+void orc_fwht128(float *v) {
+  for (int h = 1; h < 128; h *= 2)
+    for (int i = 0; i < 128; i += 2 * h)
+      for (int j = i; j < i + h; j++) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+}
+
+static float rht_norm(void) { return (float)(1.0 / sqrt(128.0)); }
+
+static int sign_bit(const uint32_t signs[4], int k) { return (signs[k >> 5] >> (k & 31)) & 1; }
+
+void orc_rht128(const float *x, const uint32_t signs[4], float *z) {
+  float w[128];
+  for (int k = 0; k < 128; k++) w[k] = sign_bit(signs, k) ? -x[k] : x[k];
+  orc_fwht128(w);
+  const float c = rht_norm();
+  for (int k = 0; k < 128; k++) z[k] = w[k] * c;
+}
+
+void orc_irht128(const float *z, const uint32_t signs[4], float *x) {
+  float w[128];
+  for (int k = 0; k < 128; k++) w[k] = z[k];
+  orc_fwht128(w);
+  const float c = rht_norm();
+  for (int k = 0; k < 128; k++) {
+    float u = w[k] * c;
+    x[k] = sign_bit(signs, k) ? -u : u;
+  }
+}
+
+/* READING (reduction order): pairwise binary tree over the indices in their
+ * natural order, sum(v[0..n)) = sum(first half) + sum(second half). */
+float orc_pairwise_sum(const float *v, int n) {
+  if (n == 1) return v[0];
+  return orc_pairwise_sum(v, n / 2) + orc_pairwise_sum(v + n / 2, n - n / 2);
+}
+
+/* ======================================================================
+ * Quantization
+ * ==================================================================== */
+
+static void put_nibble(uint8_t *codes_row, int64_t k, int nib) {
+  if (k & 1) codes_row[k >> 1] = (uint8_t)((codes_row[k >> 1] & 0x0F) | (nib << 4));
+  else codes_row[k >> 1] = (uint8_t)((codes_row[k >> 1] & 0xF0) | nib);
+}
+
+/* NVFP4 with round-to-nearest (forward pass [QII-sum "Quantisierung im
+ * Vorwaertsdurchlauf"]: one E4M3 scale per 16 elements under an fp32 tensor
+ * scale) or elementwise stochastic rounding.  One 16-block:
+ *   a_b = max |z|;  v = (a_b / 6) / s_t;  e = E4M3(v) (RNE for RTN, ceil for SR)
+ *   S = value(e) * s_t;  y = z * (1 / S);  magnitude = round(min(|y|, 6)).
+ * Pinned by: Table 1 MSE of NVFP4 on N(0,1) data [IF4 Table 1]; SR closed
+ * form [PAL]; brute-force per-element nearest search. */
+static void nvfp4_block(const float *z, float s_t, int rounding, uint64_t seed,
+                        uint32_t stream, uint64_t idx0, uint8_t *codes_row,
+                        int64_t k0, uint8_t *scale_out) {
+  float a = 0.0f;
+  for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(z[i]));
+  float v = (a / 6.0f) / s_t;
+  int e = (rounding == ORC_SR) ? orc_e4m3_ceil_sat(v) : orc_e4m3_rne_sat(v);
+  *scale_out = (uint8_t)e;
+  float r = 0.0f;
+  if (e != 0) r = 1.0f / (orc_e4m3_value(e) * s_t);
+  for (int i = 0; i < 16; i++) {
+    int mag = 0;
+    if (e != 0) {
+      float y = fminf(fabsf(z[i] * r), 6.0f);
+      if (rounding == ORC_SR)
+        mag = orc_sr_e2m1(y, orc_uniform16(seed, 0, stream, idx0 + (uint64_t)i));
+      else
+        mag = orc_e2m1_rne(y);
+    }
+    put_nibble(codes_row, k0 + i, (signbit(z[i]) ? 8 : 0) | mag);
+  }
+}
+
+/* One branch of IF4 for a 16-block: returns the scale byte, writes nibbles
+ * into nib[], and the pairwise sum of squared errors into *sse.
+ * fp branch: E2M1 values, scale a/6; int branch: integers 0..7, scale a/7
+ * (the NVINT4 row of [IF4 Table 1], maximum 7 x 448). */
+static int if4_branch(const float *z, float s_t, int is_int, int nib[16], float *sse) {
+  float a = 0.0f;
+  for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(z[i]));
+  float top = is_int ? 7.0f : 6.0f;
+  int e = orc_e4m3_rne_sat((a / top) / s_t);
+  float S = orc_e4m3_value(e) * s_t;
+  float r = (e != 0) ? 1.0f / S : 0.0f;
+  float sq[16];
+  for (int i = 0; i < 16; i++) {
+    int mag = 0;
+    if (e != 0) {
+      float y = fminf(fabsf(z[i] * r), top);
+      mag = is_int ? orc_int4_rne(y) : orc_e2m1_rne(y);
+    }
+    float val = is_int ? (float)mag : GRID_E2M1[mag];
+    if (signbit(z[i])) val = -val;
+    float d = z[i] - val * S;
+    sq[i] = d * d;
+    nib[i] = (signbit(z[i]) ? 8 : 0) | mag;
+  }
+  *sse = orc_pairwise_sum(sq, 16);
+  return e;
+}
+
+/* IF4: quantize the 16-group both ways and keep the one with the smaller
+ * squared error; the choice is the otherwise unused sign bit of the E4M3
+ * scale (set = scaled INT4) [IF4 abstract, Figure 1, Figure 3].
+ * READING: the INT branch has its own E4M3 scale a/7 under the shared tensor
+ * scale; ties keep FP4; INT nibbles are sign-magnitude (each value keeps its
+ * own sign bit [IF4 Figure 1]).
+ * Pinned by: Table 1 MSE of IF4 and NVINT4 on N(0,1) [IF4 Table 1];
+ * brute-force minimum over both branches on small blocks. */
+static void if4_block(const float *z, float s_t, int format, uint8_t *codes_row,
+                      int64_t k0, uint8_t *scale_out) {
+  int nf[16], ni[16];
+  float sse_f = 0.0f, sse_i = 0.0f;
+  int ei = if4_branch(z, s_t, 1, ni, &sse_i);
+  if (format == ORC_FMT_NVINT4) {
+    *scale_out = (uint8_t)ei;
+    for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, ni[i]);
+    return;
+  }
+  int ef = if4_branch(z, s_t, 0, nf, &sse_f);
+  int use_int = sse_i < sse_f;
+  *scale_out = (uint8_t)(use_int ? (ei | 0x80) : ef);
+  for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, use_int ? ni[i] : nf[i]);
+}
+
+/* MS-EDEN, first half, for one correction group of G elements (G = 128, the
+ * rotation group, or 16) [QII-abs; QII-sum "Kerninnovationen" and
+ * "Quantisierung im Rueckwaertsdurchlauf"]: the randomness moves from the
+ * FP4 values onto the micro-scales; a correction rescaling keeps the
+ * rotated estimate unbiased, and is folded into the group scale by SR.
+ * READING (textbook EDEN): deterministic RTN codes under the exact block
+ * scale s_b = a_b / 6; correction c = sum z^2 / sum z*zhat over the group
+ * (pairwise trees); target scale t_b = s_b * c for every block of the group.
+ * Pinned by: unbiasedness under Haar-random rotations (Monte Carlo), error
+ * ratio against SR above 2 [QII-abs], exact expectation of the scale SR. */
+static void eden_group(const float *z, int G, uint8_t *codes_row, int64_t k0, float *tb) {
+  float zz[128] = {0}, zh[128] = {0}, s_b[8] = {0};
+  for (int b = 0; b < G / 16; b++) {
+    const float *zb = z + 16 * b;
+    float a = 0.0f;
+    for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(zb[i]));
+    s_b[b] = a / 6.0f;
+    float r = (a > 0.0f) ? 1.0f / s_b[b] : 0.0f;
+    for (int i = 0; i < 16; i++) {
+      int mag = 0;
+      if (a > 0.0f) mag = orc_e2m1_rne(fminf(fabsf(zb[i] * r), 6.0f));
+      float q = GRID_E2M1[mag] * s_b[b];
+      zh[16 * b + i] = signbit(zb[i]) ? -q : q;
+      put_nibble(codes_row, k0 + 16 * b + i, (signbit(zb[i]) ? 8 : 0) | mag);
+    }
+  }
+  for (int i = 0; i < G; i++) {
+    zz[i] = z[i] * z[i];
+    zh[i] = z[i] * zh[i];
+  }
+  float N = orc_pairwise_sum(zz, G);
+  float D = orc_pairwise_sum(zh, G);
+  float c = (D > 0.0f) ? N / D : 1.0f;
+  for (int b = 0; b < G / 16; b++) tb[b] = s_b[b] * c;
+}
+
+/* View the input as the [rows_out x K] matrix whose rows are quantization
+ * groups: axis 0 keeps rows (groups run along the contiguous dimension);
+ * axis 1 transposes (groups run along the strided dimension, i.e. along the
+ * reduction dimension of a row-major activation or gradient, as the
+ * backward re-quantization of [QII-sum] requires). */
+static void make_view(const float *x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                      float *Z) {
+  if (axis == 0) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) memcpy(Z + r * cols, x + r * ld, sizeof(float) * cols);
+  } else {
+    /* Z[c][r] = x[r][c], in 64 x 64 tiles */
+#pragma omp parallel for schedule(static)
+    for (int64_t c0 = 0; c0 < cols; c0 += 64)
+      for (int64_t r0 = 0; r0 < rows; r0 += 64)
+        for (int64_t c = c0; c < c0 + 64 && c < cols; c++)
+          for (int64_t r = r0; r < r0 + 64 && r < rows; r++) Z[c * rows + r] = x[r * ld + c];
+  }
+}
+
+int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
+                 int format, int rounding, int axis, int rht,
+                 const uint32_t signs[4], uint64_t seed, uint32_t stream,
+                 int eden_group_size, const float *ts_in,
+                 uint8_t *codes, uint8_t *scales, float *ts_out,
+                 float *z_out, float *tb_out) {
+  if (!x || !codes || !scales || !ts_out) return ORC_BAD_ARG;
+  if (format < 0 || format > 2 || rounding < 0 || rounding > 2 || axis < 0 || axis > 1)
+    return ORC_BAD_ARG;
+  if (format != ORC_FMT_NVFP4 && rounding != ORC_RTN) return ORC_BAD_ARG;
+  if (rows < 0 || cols < 0 || ld < cols) return ORC_BAD_SHAPE;
+  const int64_t R = axis == 0 ? rows : cols;
+  const int64_t K = axis == 0 ? cols : rows;
+  const int G = (rounding == ORC_MSEDEN) ? eden_group_size : 16;
+  if (rounding == ORC_MSEDEN && G != 16 && G != 128) return ORC_BAD_ARG;
+  if (K % 16) return ORC_BAD_SHAPE;
+  if ((rht || G == 128) && K % 128) return ORC_BAD_SHAPE;
+  if (rht && !signs) return ORC_BAD_ARG;
+  if (R == 0 || K == 0) { *ts_out = ts_in ? *ts_in : 1.0f; return ORC_OK; }
+
+  float *Z = (float *)malloc(sizeof(float) * (size_t)(R * K));
+  if (!Z) return ORC_BAD_ARG;
+  make_view(x, rows, cols, ld, axis, Z);
+
+  /* 1. rotation of every 128-group of every row */
+  if (rht) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+      for (int64_t g = 0; g < K; g += 128) {
+        float tmp[128];
+        orc_rht128(Z + r * K + g, signs, tmp);
+        memcpy(Z + r * K + g, tmp, sizeof(tmp));
+      }
+  }
+  if (z_out) memcpy(z_out, Z, sizeof(float) * (size_t)(R * K));
+  memset(codes, 0, (size_t)(R * K / 2));
+
+  if (rounding != ORC_MSEDEN) {
+    /* 2. tensor scale: absmax over the (rotated) tensor, mapped to the
+     * largest representable magnitude [IF4 Table 1: 6 x 448 for NVFP4 and
+     * IF4, 7 x 448 for NVINT4]; an all-zero tensor takes scale 1. */
+    float s_t;
+    if (ts_in) {
+      s_t = *ts_in;
+    } else {
+      float m = 0.0f;
+#pragma omp parallel for reduction(max : m) schedule(static)
+      for (int64_t i = 0; i < R * K; i++) m = fmaxf(m, fabsf(Z[i]));
+      float top = (format == ORC_FMT_NVINT4) ? 7.0f * 448.0f : 6.0f * 448.0f;
+      s_t = (m > 0.0f) ? m / top : 1.0f;
+    }
+    *ts_out = s_t;
+    /* 3. per 16-block scale and codes */
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+      for (int64_t k = 0; k < K; k += 16) {
+        const float *zb = Z + r * K + k;
+        uint8_t *sc = scales + r * (K / 16) + k / 16;
+        if (format == ORC_FMT_NVFP4)
+          nvfp4_block(zb, s_t, rounding, seed, stream, (uint64_t)(r * K + k), codes + r * (K / 2),
+                      k, sc);
+        else
+          if4_block(zb, s_t, format, codes + r * (K / 2), k, sc);
+      }
+  } else {
+    /* MS-EDEN: codes and target scales t_b per group, then the tensor scale
+     * from the largest target, then the E4M3 scales by SR of t_b / s_t. */
+    float *tb = (float *)malloc(sizeof(float) * (size_t)(R * K / 16));
+    if (!tb) { free(Z); return ORC_BAD_ARG; }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+      for (int64_t k = 0; k < K; k += G)
+        eden_group(Z + r * K + k, G, codes + r * (K / 2), k, tb + r * (K / 16) + k / 16);
+    float s_t;
+    if (ts_in) {
+      s_t = *ts_in;
+    } else {
+      float T = 0.0f;
+#pragma omp parallel for reduction(max : T) schedule(static)
+      for (int64_t i = 0; i < R * K / 16; i++) T = fmaxf(T, tb[i]);
+      /* READING: the tensor scale maps the largest target scale to the
+       * E4M3 maximum, so the stochastic rounding of every scale stays inside
+       * the grid and keeps its expectation. */
+      s_t = (T > 0.0f) ? T / 448.0f : 1.0f;
+    }
+    *ts_out = s_t;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < R * K / 16; b++) {
+      float a = fminf(tb[b] / s_t, 448.0f);
+      scales[b] = (uint8_t)orc_sr_e4m3(a, orc_uniform16(seed, 1, stream, (uint64_t)b));
+    }
+    if (tb_out) memcpy(tb_out, tb, sizeof(float) * (size_t)(R * K / 16));
+    free(tb);
+  }
+  free(Z);
+  return ORC_OK;
+}
+
+/* ======================================================================
+ * Dequantization: value = sign * (v * (scale * s_t)), v the E2M1 value or,
+ * for IF4 groups flagged INT (scale bit 7), the integer magnitude.  With
+ * inverse-rotation signs, each 128-group is rotated back afterwards.
+ * Pinned by: round trip of exactly representable tensors; Table 1 MSE.
+ * ==================================================================== */
+int orc_dequantize(const uint8_t *codes, const uint8_t *scales, float ts,
+                   int64_t rows_out, int64_t k, int format,
+                   const uint32_t *inv_signs, float *out) {
+  if (!codes || !scales || !out) return ORC_BAD_ARG;
+  if (k % 16 || (inv_signs && k % 128)) return ORC_BAD_SHAPE;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows_out; r++) {
+    for (int64_t j = 0; j < k; j++) {
+      int byte = codes[r * (k / 2) + j / 2];
+      int nib = (j & 1) ? (byte >> 4) : (byte & 15);
+      int e = scales[r * (k / 16) + j / 16];
+      int is_int = (format == ORC_FMT_NVINT4) || (format == ORC_FMT_IF4 && (e & 0x80));
+      float S = orc_e4m3_value(e & 0x7F) * ts;
+      float v = is_int ? (float)(nib & 7) : GRID_E2M1[nib & 7];
+      float q = v * S;
+      out[r * k + j] = (nib & 8) ? -q : q;
+    }
+    if (inv_signs)
+      for (int64_t g = 0; g < k; g += 128) {
+        float tmp[128];
+        orc_irht128(out + r * k + g, inv_signs, tmp);
+        memcpy(out + r * k + g, tmp, sizeof(tmp));
+      }
+  }
+  return ORC_OK;
+}
+
+/* ======================================================================
+ * Block-scaled FP4 GEMM, plain definition: C = (s_A s_B) * A_hat B_hat^T
+ * with A_hat[m][k] = E2M1(code) * E4M3(block scale) taken exactly, both
+ * operands stored K-major.  Accumulated in fp64 (ground truth).
+ * Pinned by: a dense float64 matmul (numpy) of independently dequantized
+ * operands.
+ * ==================================================================== */
+static double operand_value(const uint8_t *codes, const uint8_t *scales, int64_t K,
+                            int format, int64_t row, int64_t k) {
+  int byte = codes[row * (K / 2) + k / 2];
+  int nib = (k & 1) ? (byte >> 4) : (byte & 15);
+  int e = scales[row * (K / 16) + k / 16];
+  int is_int = (format == ORC_FMT_NVINT4) || (format == ORC_FMT_IF4 && (e & 0x80));
+  double v = is_int ? (double)(nib & 7) : (double)GRID_E2M1[nib & 7];
+  double q = v * (double)orc_e4m3_value(e & 0x7F);
+  return (nib & 8) ? -q : q;
+}
+
+int orc_gemm_entries(const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
+                     const uint8_t *b_codes, const uint8_t *b_scales, float b_ts,
+                     int64_t M, int64_t N, int64_t K, int format,
+                     const int64_t *im, const int64_t *in, int64_t count, double *out) {
+  if (K % 16) return ORC_BAD_SHAPE;
+  for (int64_t t = 0; t < count; t++)
+    if (im[t] < 0 || im[t] >= M || in[t] < 0 || in[t] >= N) return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < count; t++) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; k++)
+      acc += operand_value(a_codes, a_scales, K, format, im[t], k) *
+             operand_value(b_codes, b_scales, K, format, in[t], k);
+    out[t] = (double)a_ts * (double)b_ts * acc;
+  }
+  return ORC_OK;
+}
+
+int orc_gemm_full(const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
+                  const uint8_t *b_codes, const uint8_t *b_scales, float b_ts,
+                  int64_t M, int64_t N, int64_t K, int format, double *out) {
+  if (K % 16) return ORC_BAD_SHAPE;
+  double *A = (double *)malloc(sizeof(double) * (size_t)(M * K));
+  double *B = (double *)malloc(sizeof(double) * (size_t)(N * K));
+  if (!A || !B) { free(A); free(B); return ORC_BAD_ARG; }
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t k = 0; k < K; k++) A[m * K + k] = operand_value(a_codes, a_scales, K, format, m, k);
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t k = 0; k < K; k++) B[n * K + k] = operand_value(b_codes, b_scales, K, format, n, k);
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t n = 0; n < N; n++) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; k++) acc += A[m * K + k] * B[n * K + k];
+      out[m * N + n] = (double)a_ts * (double)b_ts * acc;
+    }
+  free(A);
+  free(B);
+  return ORC_OK;
+}
