@@ -1,0 +1,202 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4: NVFP4 microscaled quantization of training
+ * tensors on AMD Instinct MI355X (gfx950), its IF4 variant, dequantization,
+ * and the block-scaled FP4 GEMM that consumes the packed operands.
+ *
+ * Sources (the pages the operations follow):
+ *   [QII-abs]  Quartet II: Accurate LLM Pre-Training in NVFP4 by Improved
+ *              Unbiased Gradient Estimation, abstract (OpenAlex W7127094184).
+ *   [QII-sum]  Quartet II news summary (mind-verse.de), sections
+ *              "Kerninnovationen", "Quantisierung im Rueckwaertsdurchlauf",
+ *              "Quantisierung im Vorwaertsdurchlauf".
+ *   [PAL]      "Comparing INT4 and NVFP4 Palettes on Real Gradient Tensors"
+ *              (sethwheeler.dev), opening paragraph and section "The two
+ *              corners, and what the palette does to them".
+ *   [IF4]      Adaptive Block-Scaled Data Types / IF4 (arXiv 2603.28765),
+ *              abstract, Figure 1, Table 1, Figure 3.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named x, codes, scales, tensor_scale, ws, out, a_*, b_*, c are
+ *   DEVICE pointers (HIP device memory of the current device).  The
+ *   rht_signs / inv_rht_signs arrays are HOST pointers (4 words, read during
+ *   the call).  The caller owns every buffer; the library allocates no device
+ *   memory and keeps no state between calls.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every entry point
+ *   only enqueues work on that stream and returns; it never synchronizes.
+ *   Faults inside kernels surface at the caller's next synchronization.
+ * - Return value: NVFP4_OK (0) or a negative nvfp4_status.  On error nothing
+ *   has been enqueued (validation happens before any launch), except for
+ *   NVFP4_HIP_ERROR, which reports a failed launch.  nvfp4_last_error()
+ *   returns a thread-local detail string for the last failing call.  The
+ *   library never aborts or throws across this interface.
+ * - Non-finite inputs, and tensors so small in magnitude that a block scale
+ *   times the tensor scale underflows to zero, give unspecified (but
+ *   memory-safe) results.
+ *
+ * Packed layout (the pages fix the format, not the bytes; this layout is the
+ * library's own):
+ *   codes  [rows_out x K/2] bytes, row-major; element 2j in the low nibble of
+ *          byte j, element 2j+1 in the high nibble.  Nibble = sign<<3 | mag.
+ *          NVFP4 magnitudes 0..7 index the E2M1 grid {0,.5,1,1.5,2,3,4,6}
+ *          [PAL opening paragraph]; IF4 groups flagged INT hold integers 0..7
+ *          (sign-magnitude, each value keeps its own sign [IF4 Figure 1]).
+ *   scales [rows_out x K/16] bytes, row-major, one E4M3 ("FN": bias 7, max
+ *          448, subnormals to 2^-9 [IF4 Table 1]) per 16 consecutive
+ *          elements of a row [QII-sum "Quantisierung im Vorwaertsdurchlauf"].
+ *          In IF4 output bit 7 is the INT flag [IF4 Figure 1].
+ *   tensor_scale  one fp32 on the device [QII-sum, same section].
+ *   Dequantized value = sign * (mag_value * (E4M3(scale & 0x7F) * tensor_scale)).
+ * Quantization axis: axis 0 groups run along the contiguous dimension of the
+ * row-major input x[rows][ld] and rows_out = rows, K = cols; axis 1 groups
+ * run along the strided dimension (the reduction dimension of a row-major
+ * activation or gradient, for the backward re-quantization of [QII-sum]) and
+ * the output is the transpose: rows_out = cols, K = rows.
+ * Element index (for the random streams) = row_out * K + k in the output
+ * layout; block index = element index / 16.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_INVALID_ARG = -1,   /* null pointer, bad enum, negative size          */
+  NVFP4_BAD_SHAPE = -2,     /* K % 16, K % 128 with rotation/MS-EDEN-128, ld  */
+  NVFP4_MISALIGNED = -3,    /* pointer or row stride not aligned as required  */
+  NVFP4_WS_TOO_SMALL = -4,  /* workspace smaller than nvfp4_workspace_size()  */
+  NVFP4_HIP_ERROR = -5,     /* a kernel launch failed                         */
+  NVFP4_UNSUPPORTED = -6    /* valid request this build does not implement    */
+} nvfp4_status;
+
+typedef enum nvfp4_dtype { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+
+typedef enum nvfp4_rounding {
+  NVFP4_RTN = 0,     /* round-to-nearest-even codes, RNE block scales        */
+  NVFP4_SR = 1,      /* stochastic element rounding, block scales rounded up */
+  NVFP4_MSEDEN = 2   /* MS-EDEN: RTN codes, corrected scales rounded by SR   */
+} nvfp4_rounding;
+
+typedef enum nvfp4_format { NVFP4_FORMAT_NVFP4 = 0, NVFP4_FORMAT_IF4 = 1 } nvfp4_format;
+
+typedef struct nvfp4_opts {
+  int32_t rounding;        /* nvfp4_rounding                                   */
+  int32_t axis;            /* 0 or 1, see above                                */
+  int32_t rht;             /* 1: 128-point randomized Hadamard rotation first  */
+  uint32_t rht_signs[4];   /* bit k of the 128-bit vector = bit k%32 of word
+                              k/32; set = negate coordinate k before the
+                              transform                                        */
+  uint64_t seed;           /* Philox-4x32-10 key                               */
+  uint32_t stream;         /* Philox counter word 3 (e.g. a step or trial id)  */
+  int32_t eden_group;      /* MS-EDEN correction group: 128 (default) or 16    */
+  const float *tensor_scale_in; /* DEVICE pointer to a given fp32 tensor scale,
+                              or NULL to compute it from this tensor           */
+} nvfp4_opts;
+
+/* Fills *o with defaults: RTN, axis 0, no rotation, seed 0, stream 0,
+ * eden_group 128, computed tensor scale. */
+void nvfp4_opts_init(nvfp4_opts *o);
+
+/* Bytes of device workspace the quantizers need for this shape and options
+ * (a multiple of 256; the ws pointer must be 256-byte aligned).  Holds
+ * per-workgroup partial maxima and, for MS-EDEN, one fp32 target scale per
+ * 16 elements. */
+size_t nvfp4_workspace_size(int64_t rows, int64_t cols, const nvfp4_opts *o);
+
+/*
+ * NVFP4 quantization [QII-sum "Quantisierung im Vorwaertsdurchlauf" (RTN,
+ * E4M3 per 16, fp32 per tensor); QII-abs and QII-sum "Quantisierung im
+ * Rueckwaertsdurchlauf" (stochastic rounding, randomized Hadamard rotation
+ * and MS-EDEN)].  Steps, per tensor:
+ *   1. optional rotation z = 2^-3.5 * H_128 * diag(signs) * x of every
+ *      128-group along the quantization axis (Sylvester order, stages of
+ *      stride 1, 2, ..., 64);
+ *   2. RTN/SR: tensor scale s_t = max|z| / (6 * 448) (1 if the tensor is 0);
+ *      per 16-block a = max|z|, scale e = E4M3((a/6)/s_t) rounded to nearest
+ *      even (RTN) or up (SR); codes = round(min(|z| / (e*s_t), 6)) on the
+ *      E2M1 grid, to nearest even (RTN) or stochastically (SR, Philox tag 0,
+ *      one 16-bit uniform per element);
+ *   3. MS-EDEN: codes by RTN under the exact scale a/6; per correction group
+ *      c = sum z^2 / sum z*zhat; target t = (a/6)*c; s_t = max t / 448;
+ *      scale e = SR of min(t/s_t, 448) onto the E4M3 grid (Philox tag 1,
+ *      one uniform per block).
+ * x: device, in_dtype elements, row-major with leading dimension ld >= cols
+ * (elements).  axis 0 needs a 16-byte aligned base and ld * sizeof(elem) a
+ * multiple of 16; axis 1 needs only element alignment (16-byte aligned rows
+ * are loaded with vector loads, others element by element).
+ * codes / scales: device, 16-byte aligned, sizes as in the layout above.
+ * tensor_scale: device fp32 written with s_t (copied from tensor_scale_in if
+ * given).  ws: device workspace of at least nvfp4_workspace_size() bytes,
+ * 256-byte aligned; its contents on entry are ignored.
+ * Shape rules: K % 16 == 0; K % 128 == 0 with rotation or MS-EDEN group 128.
+ */
+int nvfp4_quantize_nvfp4(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                         const nvfp4_opts *o, uint8_t *codes, uint8_t *scales,
+                         float *tensor_scale, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * IF4 quantization [IF4 abstract, Figure 1, Figure 3]: every 16-group is
+ * quantized as NVFP4 (E2M1 under scale a/6) and as scaled INT4 (integers
+ * 0..7 under its own scale a/7, both RNE), and keeps the one with the
+ * smaller sum of squared errors (ties keep FP4); the INT choice sets bit 7
+ * of the scale byte.  Tensor scale s_t = max|z| / (6 * 448).  Same arguments
+ * and layout rules as nvfp4_quantize_nvfp4; o->rounding must be NVFP4_RTN.
+ */
+int nvfp4_quantize_if4(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                       const nvfp4_opts *o, uint8_t *codes, uint8_t *scales,
+                       float *tensor_scale, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dequantization, the inverse of the encodings above: out[r][k] =
+ * sign * (v * (E4M3(scale & 0x7F) * tensor_scale)), v the E2M1 value or, for
+ * IF4 groups with bit 7 set, the integer magnitude; then, if inv_rht_signs is
+ * not NULL, the inverse rotation signs * (2^-3.5 * H_128 * z) of every
+ * 128-group.  codes/scales/tensor_scale: device, as produced above;
+ * inv_rht_signs: HOST, 4 words, or NULL.  out: device, [rows_out x k],
+ * out_dtype (fp32, or bf16 rounded to nearest even), 16-byte aligned.
+ * k % 16 == 0 (k % 128 == 0 with inverse rotation).
+ */
+int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                     int64_t rows_out, int64_t k, int format, const uint32_t *inv_rht_signs,
+                     int out_dtype, void *out, void *stream);
+
+/*
+ * Block-scaled FP4 GEMM [QII-sum "Kerninnovationen" (NVFP4 GEMMs for linear
+ * layers); QII-abs]:  C[M x N] = (ts_a * ts_b) * sum_k A[m][k] * B[n][k], with
+ * A[m][k] = E2M1(code) * E4M3(scale) taken exactly, both operands K-major
+ * packed NVFP4 as produced by nvfp4_quantize_nvfp4 (A: rows_out = M, B:
+ * rows_out = N, both with the same K).  Accumulation in fp32 on the matrix
+ * cores; the dequantized operands are exact in fp16, so the only rounding is
+ * the accumulation's.  c: device, [M x ldc] row-major, out_dtype fp32 or bf16,
+ * ldc >= N.  a_ts, b_ts: device fp32 tensor scales.  K % 16 == 0; codes and
+ * scales 16-byte aligned.  IF4 operands are rejected (NVFP4_UNSUPPORTED).
+ */
+int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                     const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+                     int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
+                     void *stream);
+
+/*
+ * The rotation alone, for checking it: out[rows_out x K] fp32 = the rotated
+ * values of step 1 of nvfp4_quantize_nvfp4, in the output layout of `axis`.
+ * Same x rules; K % 128 == 0; out device, 16-byte aligned.
+ */
+int nvfp4_rht(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
+              const uint32_t *rht_signs, float *out, void *stream);
+
+const char *nvfp4_status_string(int status);
+const char *nvfp4_last_error(void);
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

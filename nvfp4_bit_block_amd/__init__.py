@@ -1,0 +1,267 @@
+"""nvfp4_bit_block_amd -- NVFP4 microscaled quantization (randomized Hadamard
+rotation, RTN, stochastic rounding, MS-EDEN), IF4, dequantization and the
+block-scaled FP4 GEMM on AMD Instinct MI355X (gfx950).
+
+This module is argument marshalling over the C ABI of ``libnvfp4.so``
+(``include/nvfp4.h``): PyTorch provides device memory and the current HIP
+stream, every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: without the built library (or without a GPU) every
+compute call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "RTN", "SR", "MSEDEN", "FORMAT_NVFP4", "FORMAT_IF4", "QTensor", "NvFp4Error",
+    "lib", "signs_to_words", "workspace_size", "quantize_nvfp4", "quantize_if4",
+    "dequantize", "gemm_nvfp4", "rht", "abi_version",
+]
+
+RTN, SR, MSEDEN = 0, 1, 2
+FORMAT_NVFP4, FORMAT_IF4 = 0, 1
+_F32, _BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+_ROUNDING = {"rtn": RTN, "sr": SR, "mseden": MSEDEN, "ms-eden": MSEDEN, RTN: RTN, SR: SR,
+             MSEDEN: MSEDEN}
+
+
+class NvFp4Error(RuntimeError):
+    pass
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [
+        ("rounding", ctypes.c_int32),
+        ("axis", ctypes.c_int32),
+        ("rht", ctypes.c_int32),
+        ("rht_signs", ctypes.c_uint32 * 4),
+        ("seed", ctypes.c_uint64),
+        ("stream", ctypes.c_uint32),
+        ("eden_group", ctypes.c_int32),
+        ("tensor_scale_in", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libnvfp4.so (built by ``nvfp4_bit_block_amd.build``).  Import
+    torch first so that the library binds to torch's HIP runtime."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NvFp4Error(f"{LIB_PATH} is missing: build it with `python -m nvfp4_bit_block_amd.build`"
+                         " (or __graft_entry__.build())")
+    import torch  # noqa: F401  (binds the HIP runtime before the library loads)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, INT, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nvfp4_opts_init.restype = None
+    L.nvfp4_opts_init.argtypes = [ctypes.POINTER(_Opts)]
+    L.nvfp4_workspace_size.restype = SZ
+    L.nvfp4_workspace_size.argtypes = [I64, I64, ctypes.POINTER(_Opts)]
+    for name in ("nvfp4_quantize_nvfp4", "nvfp4_quantize_if4"):
+        f = getattr(L, name)
+        f.restype = INT
+        f.argtypes = [P, INT, I64, I64, I64, ctypes.POINTER(_Opts), P, P, P, P, SZ, P]
+    L.nvfp4_dequantize.restype = INT
+    L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, INT, P, INT, P, P]
+    L.nvfp4_gemm_nvfp4.restype = INT
+    L.nvfp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, INT, I64, P]
+    L.nvfp4_rht.restype = INT
+    L.nvfp4_rht.argtypes = [P, INT, I64, I64, I64, INT, P, P, P]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_status_string.argtypes = [INT]
+    L.nvfp4_last_error.restype = ctypes.c_char_p
+    L.nvfp4_last_error.argtypes = []
+    L.nvfp4_abi_version.restype = INT
+    L.nvfp4_abi_version.argtypes = []
+    _lib = L
+    return L
+
+
+def abi_version():
+    return int(lib().nvfp4_abi_version())
+
+
+def _check(rc):
+    if rc != 0:
+        L = lib()
+        raise NvFp4Error(f"{L.nvfp4_status_string(rc).decode()} ({rc}): {L.nvfp4_last_error().decode()}")
+
+
+def signs_to_words(signs):
+    """128 flags (1 = negate) or 4 uint32 words -> 4 uint32 words (bit k of
+    the vector is bit k % 32 of word k // 32)."""
+    a = np.asarray(signs)
+    if a.size == 4 and a.dtype != np.uint8:
+        return np.ascontiguousarray(a, dtype=np.uint32)
+    a = a.astype(np.uint8).reshape(128)
+    w = np.zeros(4, dtype=np.uint32)
+    for k in np.flatnonzero(a):
+        w[k // 32] |= np.uint32(1 << (k % 32))
+    return w
+
+
+def _stream(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t, torch):
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise NvFp4Error(f"input dtype {t.dtype} is not float32 or bfloat16")
+
+
+def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in):
+    o = _Opts()
+    lib().nvfp4_opts_init(ctypes.byref(o))
+    o.rounding = _ROUNDING[rounding.lower() if isinstance(rounding, str) else rounding]
+    o.axis = int(axis)
+    if rht_signs is not None:
+        o.rht = 1
+        w = signs_to_words(rht_signs)
+        for i in range(4):
+            o.rht_signs[i] = int(w[i])
+    o.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    o.stream = int(stream_id) & 0xFFFFFFFF
+    o.eden_group = int(eden_group)
+    o.tensor_scale_in = None if tensor_scale_in is None else tensor_scale_in.data_ptr()
+    return o
+
+
+@dataclass
+class QTensor:
+    """Packed NVFP4 / IF4 tensor in the library's layout: codes [rows_out,
+    K/2] uint8 (low nibble = even element), scales [rows_out, K/16] uint8
+    (E4M3, bit 7 = INT flag for IF4), tensor scale [1] float32 -- all on the
+    device."""
+    codes: "object"
+    scales: "object"
+    tensor_scale: "object"
+    format: int = FORMAT_NVFP4
+
+    @property
+    def rows(self):
+        return self.codes.shape[0]
+
+    @property
+    def k(self):
+        return self.codes.shape[1] * 2
+
+
+def workspace_size(rows, cols, rounding=RTN, axis=0, tensor_scale_in=None):
+    o = _opts(rounding, axis, None, 0, 0, 128, tensor_scale_in)
+    return int(lib().nvfp4_workspace_size(int(rows), int(cols), ctypes.byref(o)))
+
+
+def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in,
+              out, workspace, fmt):
+    import torch
+    L = lib()
+    if x.dim() != 2:
+        raise NvFp4Error("x must be 2-D")
+    if not x.is_cuda:
+        raise NvFp4Error("x must be a device tensor")
+    if x.stride(1) != 1:
+        raise NvFp4Error("x must have unit stride along its last dimension")
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else cols
+    o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in)
+    R, K = (rows, cols) if axis == 0 else (cols, rows)
+    dev = x.device
+    if out is None:
+        out = QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                      torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
+                      torch.empty(1, dtype=torch.float32, device=dev), fmt)
+    else:
+        out.format = fmt
+    wsz = int(L.nvfp4_workspace_size(rows, cols, ctypes.byref(o)))
+    if workspace is None or workspace.numel() < wsz:
+        workspace = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+    rc = fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld, ctypes.byref(o),
+            ctypes.c_void_p(out.codes.data_ptr()), ctypes.c_void_p(out.scales.data_ptr()),
+            ctypes.c_void_p(out.tensor_scale.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel(), _stream(torch))
+    _check(rc)
+    return out
+
+
+def quantize_nvfp4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0, eden_group=128,
+                   tensor_scale_in=None, out=None, workspace=None):
+    """NVFP4 quantization of a 2-D float32/bfloat16 device tensor (see
+    ``nvfp4_quantize_nvfp4`` in include/nvfp4.h).  rht_signs: 128 flags or 4
+    words enable the randomized Hadamard rotation.  Returns a QTensor."""
+    return _quantize(lib().nvfp4_quantize_nvfp4, x, rounding, axis, rht_signs, seed, stream_id,
+                     eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4)
+
+
+def quantize_if4(x, axis=0, rht_signs=None, tensor_scale_in=None, out=None, workspace=None):
+    """IF4 quantization (per-16 FP4/INT4 choice by lower squared error)."""
+    return _quantize(lib().nvfp4_quantize_if4, x, RTN, axis, rht_signs, 0, 0, 128, tensor_scale_in,
+                     out, workspace, FORMAT_IF4)
+
+
+def dequantize(q, inv_rht_signs=None, out_dtype=None, out=None):
+    """Decode a QTensor to [rows_out, K] float32 (or bfloat16), optionally
+    undoing the rotation."""
+    import torch
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((q.rows, q.k), dtype=out_dtype, device=q.codes.device)
+    w = None
+    if inv_rht_signs is not None:
+        w = signs_to_words(inv_rht_signs)
+    rc = lib().nvfp4_dequantize(ctypes.c_void_p(q.codes.data_ptr()), ctypes.c_void_p(q.scales.data_ptr()),
+                                ctypes.c_void_p(q.tensor_scale.data_ptr()), q.rows, q.k, q.format,
+                                None if w is None else w.ctypes.data_as(ctypes.c_void_p),
+                                _dtype_code(out, torch), ctypes.c_void_p(out.data_ptr()), _stream(torch))
+    _check(rc)
+    return out
+
+
+def gemm_nvfp4(a, b, out_dtype=None, out=None):
+    """C = (ts_a ts_b) * A_hat @ B_hat^T for two K-major NVFP4 QTensors
+    (A: [M, K], B: [N, K]); C is [M, N] float32 (or bfloat16)."""
+    import torch
+    if a.k != b.k:
+        raise NvFp4Error(f"K mismatch: {a.k} vs {b.k}")
+    if a.format != FORMAT_NVFP4 or b.format != FORMAT_NVFP4:
+        raise NvFp4Error("gemm_nvfp4 takes NVFP4 operands only")
+    out_dtype = out_dtype or torch.float32
+    M, N = a.rows, b.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    ldc = out.stride(0) if M > 1 else N
+    rc = lib().nvfp4_gemm_nvfp4(ctypes.c_void_p(a.codes.data_ptr()), ctypes.c_void_p(a.scales.data_ptr()),
+                                ctypes.c_void_p(a.tensor_scale.data_ptr()),
+                                ctypes.c_void_p(b.codes.data_ptr()), ctypes.c_void_p(b.scales.data_ptr()),
+                                ctypes.c_void_p(b.tensor_scale.data_ptr()), M, N, a.k,
+                                ctypes.c_void_p(out.data_ptr()), _dtype_code(out, torch), ldc,
+                                _stream(torch))
+    _check(rc)
+    return out
+
+
+def rht(x, signs, axis=0, out=None):
+    """The rotation step alone: rotated fp32 values [rows_out, K]."""
+    import torch
+    rows, cols = x.shape
+    R, K = (rows, cols) if axis == 0 else (cols, rows)
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.float32, device=x.device)
+    w = signs_to_words(signs)
+    ld = x.stride(0) if rows > 1 else cols
+    rc = lib().nvfp4_rht(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld, int(axis),
+                         w.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(out.data_ptr()), _stream(torch))
+    _check(rc)
+    return out

@@ -1,0 +1,262 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libnvfp4:
+// bf16 unpacking, the Philox-4x32-10 counter-based generator, E4M3 / E2M1
+// conversions, fast unsigned division, wave reductions and the 8-lane
+// 128-point Hadamard rotation.
+//
+// Arithmetic follows the library's contract: fp32, one rounding per written
+// operation (built with -ffp-contract=off), correctly rounded division,
+// denormals kept.  Every conversion below is an exact power-of-two scaling
+// followed by a single integer rounding, so each rounding decision is taken
+// on exactly representable quantities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nv4 {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bits
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 2^e as an fp32 for e in [-126, 127].
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// floor(log2(v)) for finite v >= 0, clamped from below at lo (v = 0 -> lo).
+__device__ __forceinline__ int ilog2_floor_clamped(float v, int lo) {
+  int e = (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;
+  return e < lo ? lo : e;
+}
+
+// ---------------------------------------------------------------- E4M3
+// E4M3 "FN" (bias 7, max 448, subnormals down to 2^-9).  For a value v >= 0
+// with binade E = max(floor(log2 v), -6), the representable neighbours are
+// integers q in [0, 16] times 2^(E-3); the byte is (E + 6) * 8 + q (q = 16
+// rolls into the next binade, q <= 8 covers the subnormals).
+
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
+  float sig = (float)(e ? (8u + m) : m);
+  return sig * pow2i((int)(e ? e : 1u) - 10);
+}
+
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  int E = ilog2_floor_clamped(v, -6);
+  float q = rintf(v * pow2i(3 - E));
+  return (uint32_t)((E + 6) * 8 + (int)q);
+}
+
+__device__ __forceinline__ uint32_t e4m3_ceil_sat(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  int E = ilog2_floor_clamped(v, -6);
+  float q = ceilf(v * pow2i(3 - E));
+  return (uint32_t)((E + 6) * 8 + (int)q);
+}
+
+// Stochastic rounding onto the E4M3 grid: up iff u16 < frac * 65536, where
+// frac is the (exact) position inside the bracketing gap.
+__device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
+  if (!(a > 0.0f)) return 0u;
+  if (a >= 448.0f) return 0x7Eu;
+  int E = ilog2_floor_clamped(a, -6);
+  float y = a * pow2i(3 - E);
+  float f = floorf(y);
+  float p = y - f;
+  int up = ((float)u16 < p * 65536.0f) ? 1 : 0;
+  return (uint32_t)((E + 6) * 8 + (int)f + up);
+}
+
+// ---------------------------------------------------------------- E2M1
+// E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: for a in [0, 6] with binade
+// E = max(floor(log2 a), 0), neighbours are integers q in [0, 4] times
+// 2^(E-1) and the magnitude code is 2E + q.
+
+struct E2m1 {
+  uint32_t code;
+  float value;
+};
+
+// Round to nearest, ties to the even code; a must already be clipped to 6.
+__device__ __forceinline__ E2m1 e2m1_rne(float a) {
+  int E = ilog2_floor_clamped(a, 0);
+  float q = rintf(a * pow2i(1 - E));
+  E2m1 r;
+  r.code = (uint32_t)(2 * E + (int)q);
+  r.value = q * pow2i(E - 1);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t u16) {
+  if (a >= 6.0f) return 7u;
+  int E = ilog2_floor_clamped(a, 0);
+  float y = a * pow2i(1 - E);
+  float f = floorf(y);
+  float p = y - f;
+  int up = ((float)u16 < p * 65536.0f) ? 1 : 0;
+  return (uint32_t)(2 * E + (int)f + up);
+}
+
+// Value of a magnitude code 0..7.
+__device__ __forceinline__ float e2m1_value(uint32_t mag) {
+  return (mag < 2u) ? 0.5f * (float)mag : (float)(2u + (mag & 1u)) * pow2i((int)(mag >> 1) - 2);
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox-4x32 with 10 rounds (Salmon et al., SC'11): per round the words 0
+// and 2 are multiplied by the round multipliers; the new state is
+// (hi(w2*M1) ^ w1 ^ k0, lo(w2*M1), hi(w0*M0) ^ w3 ^ k1, lo(w0*M0)), and the
+// key advances by the Weyl increments between rounds.
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t lo1 = 0xCD9E8D57u * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  Philox4 o;
+  o.w[0] = c0;
+  o.w[1] = c1;
+  o.w[2] = c2;
+  o.w[3] = c3;
+  return o;
+}
+
+// Eight 16-bit uniforms for indices 8*call .. 8*call+7 of one stream:
+// counter (call lo, call hi, tag, stream), key (seed lo, seed hi); uniform j
+// is half (j & 1) of word j >> 1.
+struct RngKey {
+  uint32_t seed_lo, seed_hi, stream;
+};
+
+__device__ __forceinline__ Philox4 uniforms8(const RngKey &k, uint64_t call, uint32_t tag) {
+  return philox4x32_10((uint32_t)call, (uint32_t)(call >> 32), tag, k.stream, k.seed_lo,
+                       k.seed_hi);
+}
+
+__device__ __forceinline__ uint32_t uniform_at(const Philox4 &p, int j) {
+  return (p.w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+// ---------------------------------------------------------------- division
+// Unsigned division by a runtime constant d >= 1 for numerators n < 2^31:
+// q = (umulhi(n, m) + n) >> s with s = ceil(log2 d), m = 2^32 (2^s - d)/d + 1.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+__host__ inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ---------------------------------------------------------------- lanes
+template <int S>
+__device__ __forceinline__ float lane_xor(float v) {
+  return __shfl_xor(v, S, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, kWave));
+  return v;
+}
+
+// Max over a workgroup of `nthreads` threads (multiple of 64); result valid
+// in every thread.  `red` must hold nthreads / 64 floats of LDS.
+__device__ __forceinline__ float block_max(float v, float *red, int nthreads) {
+  v = wave_max(v);
+  const int wid = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[wid] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int i = 1; i < nthreads / kWave; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// ---------------------------------------------------------------- rotation
+// In-lane stages (strides 1, 2, 4, 8) of the Sylvester fast Hadamard
+// transform on 16 consecutive coordinates: (a, b) -> (a + b, a - b).
+__device__ __forceinline__ void fwht16_inlane(float v[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// One cross-lane stage: lanes l and l ^ S hold coordinate blocks that are
+// 16*S apart; the lower one keeps a + b, the upper one a - b (a = lower).
+template <int S>
+__device__ __forceinline__ void fwht_cross(float v[16], uint32_t lane_in_group) {
+  const bool upper = (lane_in_group & S) != 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = lane_xor<S>(v[i]);
+    const float own = upper ? -v[i] : v[i];
+    v[i] = p + own;
+  }
+}
+
+// The rotation of a 128-group held by 8 consecutive lanes (16 consecutive
+// coordinates each, lane_in_group = position): stages of stride 1, ..., 64
+// in that order, then the 1/sqrt(128) normalization.  The sign flips are
+// applied by the caller before this.
+__device__ __forceinline__ void fwht128_group(float v[16], uint32_t lane_in_group) {
+  fwht16_inlane(v);
+  fwht_cross<1>(v, lane_in_group);
+  fwht_cross<2>(v, lane_in_group);
+  fwht_cross<4>(v, lane_in_group);
+  const float c = 0x1.6a09e6p-4f;  // fp32(1/sqrt(128)) = 0x3DB504F3
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = v[i] * c;
+}
+
+// 16 sign bits of a lane's coordinate block within the 128-bit sign vector.
+__device__ __forceinline__ uint32_t lane_sign_bits(const uint32_t sg[4], uint32_t lane_in_group) {
+  const uint32_t w = sg[lane_in_group >> 1];
+  return (w >> (16 * (lane_in_group & 1))) & 0xFFFFu;
+}
+
+// Pairwise tree over 16 values in natural order.
+__device__ __forceinline__ float tree16(const float v[16]) {
+  float s8[8], s4[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s8[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s4[i] = s8[2 * i] + s8[2 * i + 1];
+  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+}  // namespace nv4

@@ -1,0 +1,81 @@
+// kernels.hpp -- launch interface between the C ABI (api.cpp) and the gfx950
+// kernels.  Internal to libnvfp4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace nv4 {
+
+enum Mode : int {
+  kAmax = 0,       // rotated-or-raw absmax only -> per-workgroup partial maxima
+  kRtn = 1,        // NVFP4 round-to-nearest
+  kSr = 2,         // NVFP4 stochastic rounding
+  kIf4 = 3,        // IF4 selection (RTN in both branches)
+  kEden = 4,       // MS-EDEN pass 1: codes + target scales + partial maxima
+  kEdenFused = 5,  // MS-EDEN with a given tensor scale: codes + scales in one pass
+  kRot = 6         // rotation only: rotated fp32 values
+};
+
+constexpr int kThreads = 256;      // threads per workgroup of every quantizer
+constexpr int kMaxPartials = 2048; // workgroups of a pass that writes partials
+constexpr size_t kPartialBytes = 16384;
+
+struct QuantParams {
+  const void *x;
+  int64_t ld;         // input leading dimension (elements)
+  int vec;            // rows are 16-byte aligned: vector loads allowed
+  uint32_t rows, cols;  // input shape
+  uint32_t R, K;        // output rows, output row length
+  uint32_t K16;         // K / 16
+  uint32_t nblocks;     // R * K16
+  FastDiv k16div;       // division by K16 (axis 0)
+  FastDiv ctiles_div;   // division by the number of column tiles (axis 1)
+  uint32_t ntiles;      // axis 1 tile count
+  uint8_t *codes;
+  uint8_t *scales;
+  float *ts_out;
+  float *partial;       // kMaxPartials floats of workspace
+  uint32_t npartial;    // partial maxima written by the previous pass
+  float *tb;            // MS-EDEN target scales, nblocks floats of workspace
+  const float *ts_in;   // given tensor scale or nullptr
+  float *rot_out;       // kRot output
+  uint32_t sg[4];       // rotation sign words
+  int rht;
+  int group16;          // MS-EDEN correction group of 16 instead of 128
+  float top;            // largest magnitude times 448 (tensor scale divisor)
+  RngKey key;
+};
+
+// in_bf16: 1 = bf16 input, 0 = fp32 input.
+hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, uint32_t grid,
+                        hipStream_t s);
+hipError_t launch_eden_scales(const QuantParams &p, uint32_t grid, hipStream_t s);
+uint32_t quant_grid(const QuantParams &p, int in_bf16, int axis);
+uint32_t eden_scales_grid(const QuantParams &p);
+
+struct DequantParams {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const float *ts;
+  void *out;
+  uint32_t R, K, K16, nblocks;
+  uint32_t sg[4];
+  int inv_rht;
+  int if4;
+};
+hipError_t launch_dequant(const DequantParams &p, int out_bf16, hipStream_t s);
+
+struct GemmParams {
+  const uint8_t *a_codes, *a_scales;
+  const uint8_t *b_codes, *b_scales;
+  const float *a_ts, *b_ts;
+  void *c;
+  int64_t ldc;
+  uint32_t M, N, K;
+};
+hipError_t launch_gemm(const GemmParams &p, int out_bf16, hipStream_t s);
+
+}  // namespace nv4

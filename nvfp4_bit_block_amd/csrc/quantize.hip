@@ -1,0 +1,482 @@
+// quantize.hip -- NVFP4 / MS-EDEN / IF4 quantizers for gfx950.
+//
+// Sources: Quartet II abstract and news summary (mind-verse.de) for the
+// forward RTN scheme, stochastic rounding, the randomized Hadamard rotation
+// and MS-EDEN; "Comparing INT4 and NVFP4 Palettes on Real Gradient Tensors"
+// (opening paragraph) for the E2M1 grid and the SR corner; the IF4 page
+// (arXiv 2603.28765: abstract, Figure 1, Table 1, Figure 3) for E4M3 ranges
+// and the per-group FP4/INT4 selection.
+//
+// Work decomposition: one lane owns one 16-element block (one E4M3 scale) of
+// the OUTPUT layout; a 128-point rotation group is 8 consecutive lanes.
+//   axis 0: a block is 16 contiguous input elements (two 16-byte loads for
+//           bf16), addressed by the flat block index.
+//   axis 1: a workgroup stages a 256 (reduction) x 128-byte (columns) tile
+//           of the row-major input in LDS, transposed, so that each lane
+//           reads its block's 16 strided elements as contiguous LDS words.
+// A pass that needs the tensor-wide maximum writes one partial maximum per
+// workgroup into the workspace; the next pass reduces those partials in every
+// workgroup (no atomics, no memset, deterministic).
+#include <type_traits>
+
+#include "kernels.hpp"
+
+namespace nv4 {
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float tensor_scale(const QuantParams &p, float *red) {
+  if (p.ts_in) return *p.ts_in;
+  float m = 0.0f;
+  for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.partial[i]);
+  m = block_max(m, red, kThreads);
+  return (m > 0.0f) ? m / p.top : 1.0f;
+}
+
+// Sign masks for a lane's 16 coordinates: word w of the bf16 pairs gets bit
+// 15 (element 2w) and bit 31 (element 2w+1); fp32 word i gets bit 31.
+struct SignMasks {
+  uint32_t m[16];
+};
+
+template <int IN_BF16>
+__device__ __forceinline__ SignMasks make_masks(const QuantParams &p, uint32_t lig) {
+  SignMasks s;
+  const uint32_t bits = p.rht ? lane_sign_bits(p.sg, lig) : 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (IN_BF16)
+      s.m[i] = (i < 8) ? ((((bits >> (2 * i)) & 1u) << 15) | (((bits >> (2 * i + 1)) & 1u) << 31))
+                       : 0u;
+    else
+      s.m[i] = ((bits >> i) & 1u) << 31;
+  }
+  return s;
+}
+
+// 16 values from 8 words of bf16 pairs (low half = even element).
+__device__ __forceinline__ void unpack_bf16(const uint32_t w[8], const SignMasks &sm, float z[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t v = w[i] ^ sm.m[i];
+    z[2 * i] = bf16_lo(v);
+    z[2 * i + 1] = bf16_hi(v);
+  }
+}
+
+__device__ __forceinline__ void unpack_f32(const uint32_t w[16], const SignMasks &sm, float z[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = __uint_as_float(w[i] ^ sm.m[i]);
+}
+
+__device__ __forceinline__ uint32_t sign_nib(float z) { return (__float_as_uint(z) >> 28) & 8u; }
+
+__device__ __forceinline__ void store_codes(const QuantParams &p, uint32_t gb, uint32_t lo,
+                                            uint32_t hi) {
+  *reinterpret_cast<uint2 *>(p.codes + (size_t)gb * 8) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------- one block
+// z: the lane's 16 (rotated) values; gb: block index in the output layout.
+// Must be called by every lane of a wave (the MS-EDEN correction of a
+// 128-group reduces over 8 lanes); `active` gates the stores.
+template <int MODE>
+__device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool active,
+                                            const QuantParams &p, float s_t, float &lmax) {
+  if constexpr (MODE == kRot) {
+    if (active) {
+      float4 *o = reinterpret_cast<float4 *>(p.rot_out + (size_t)gb * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = make_float4(z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]);
+    }
+    return;
+  } else {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(z[i]));
+
+    if constexpr (MODE == kAmax) {
+      lmax = fmaxf(lmax, a);
+    } else if constexpr (MODE == kRtn || MODE == kSr) {
+      // scale e = E4M3((a/6)/s_t), RNE (RTN) or rounded up (SR); codes of
+      // min(|z| / (e * s_t), 6) on the E2M1 grid.
+      const float v = (a / 6.0f) / s_t;
+      const uint32_t e = (MODE == kRtn) ? e4m3_rne_sat(v) : e4m3_ceil_sat(v);
+      const float r = e ? 1.0f / (e4m3_value(e) * s_t) : 0.0f;
+      Philox4 u0, u1;
+      if constexpr (MODE == kSr) {
+        u0 = uniforms8(p.key, (uint64_t)gb * 2u, 0u);
+        u1 = uniforms8(p.key, (uint64_t)gb * 2u + 1u, 0u);
+      }
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float y = fminf(fabsf(z[i] * r), 6.0f);
+        uint32_t mag = 0;
+        if (e) {
+          if constexpr (MODE == kRtn)
+            mag = e2m1_rne(y).code;
+          else
+            mag = e2m1_sr(y, uniform_at(i < 8 ? u0 : u1, i & 7));
+        }
+        const uint32_t nib = sign_nib(z[i]) | mag;
+        if (i < 8) lo |= nib << (4 * i);
+        else hi |= nib << (4 * (i - 8));
+      }
+      if (active) {
+        store_codes(p, gb, lo, hi);
+        p.scales[gb] = (uint8_t)e;
+      }
+    } else if constexpr (MODE == kIf4) {
+      // both branches at their own scales; keep the smaller pairwise SSE.
+      const uint32_t ef = e4m3_rne_sat((a / 6.0f) / s_t);
+      const float Sf = e4m3_value(ef) * s_t;
+      const float rf = ef ? 1.0f / Sf : 0.0f;
+      const uint32_t ei = e4m3_rne_sat((a / 7.0f) / s_t);
+      const float Si = e4m3_value(ei) * s_t;
+      const float ri = ei ? 1.0f / Si : 0.0f;
+      float sqf[16], sqi[16];
+      uint32_t flo = 0, fhi = 0, ilo = 0, ihi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t sn = sign_nib(z[i]);
+        uint32_t mf = 0;
+        float vf = 0.0f;
+        if (ef) {
+          const E2m1 q = e2m1_rne(fminf(fabsf(z[i] * rf), 6.0f));
+          mf = q.code;
+          vf = q.value;
+        }
+        const float df = z[i] - (sn ? -vf : vf) * Sf;
+        sqf[i] = df * df;
+        uint32_t mi = 0;
+        if (ei) mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
+        const float vi = (float)mi;
+        const float di = z[i] - (sn ? -vi : vi) * Si;
+        sqi[i] = di * di;
+        if (i < 8) {
+          flo |= (sn | mf) << (4 * i);
+          ilo |= (sn | mi) << (4 * i);
+        } else {
+          fhi |= (sn | mf) << (4 * (i - 8));
+          ihi |= (sn | mi) << (4 * (i - 8));
+        }
+      }
+      const bool use_int = tree16(sqi) < tree16(sqf);
+      if (active) {
+        store_codes(p, gb, use_int ? ilo : flo, use_int ? ihi : fhi);
+        p.scales[gb] = (uint8_t)(use_int ? (ei | 0x80u) : ef);
+      }
+    } else if constexpr (MODE == kEden || MODE == kEdenFused) {
+      // RTN codes under the exact scale a/6; correction c = sum z^2 /
+      // sum z*zhat over the group; target t = (a/6) * c.
+      const float s_b = a / 6.0f;
+      const float r = (a > 0.0f) ? 1.0f / s_b : 0.0f;
+      float nn[16], dd[16];
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t mag = 0;
+        float val = 0.0f;
+        if (a > 0.0f) {
+          const E2m1 q = e2m1_rne(fminf(fabsf(z[i] * r), 6.0f));
+          mag = q.code;
+          val = q.value;
+        }
+        const uint32_t sn = sign_nib(z[i]);
+        const float qv = val * s_b;
+        const float zh = sn ? -qv : qv;
+        nn[i] = z[i] * z[i];
+        dd[i] = z[i] * zh;
+        if (i < 8) lo |= (sn | mag) << (4 * i);
+        else hi |= (sn | mag) << (4 * (i - 8));
+      }
+      float N = tree16(nn), D = tree16(dd);
+      if (!p.group16) {
+        N = N + lane_xor<1>(N);
+        D = D + lane_xor<1>(D);
+        N = N + lane_xor<2>(N);
+        D = D + lane_xor<2>(D);
+        N = N + lane_xor<4>(N);
+        D = D + lane_xor<4>(D);
+      }
+      const float c = (D > 0.0f) ? N / D : 1.0f;
+      const float t = s_b * c;
+      if constexpr (MODE == kEden) {
+        if (active) {
+          store_codes(p, gb, lo, hi);
+          p.tb[gb] = t;
+          lmax = fmaxf(lmax, t);
+        }
+      } else {
+        const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);
+        const uint32_t e = e4m3_sr_sat(fminf(t / s_t, 448.0f), uniform_at(u, (int)(gb & 7u)));
+        if (active) {
+          store_codes(p, gb, lo, hi);
+          p.scales[gb] = (uint8_t)e;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- axis 0
+template <int IN_BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
+  __shared__ float red[kThreads / kWave];
+  float s_t = 1.0f;
+  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kEdenFused) {
+    s_t = tensor_scale(p, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  }
+  const uint32_t lig = threadIdx.x & 7u;
+  const SignMasks sm = make_masks<IN_BF16>(p, lig);
+  float lmax = 0.0f;
+  for (uint32_t base = blockIdx.x * kThreads; base < p.nblocks; base += gridDim.x * kThreads) {
+    const uint32_t gb = base + threadIdx.x;
+    const bool active = gb < p.nblocks;
+    float z[16];
+    if (active) {
+      const uint32_t r = fdiv(gb, p.k16div);
+      const uint32_t kb = gb - r * p.K16;
+      if (IN_BF16) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            static_cast<const uint16_t *>(p.x) + (size_t)r * p.ld + (size_t)kb * 16);
+        const uint4 a0 = src[0], a1 = src[1];
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        unpack_bf16(w, sm, z);
+      } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            static_cast<const float *>(p.x) + (size_t)r * p.ld + (size_t)kb * 16);
+        const uint4 a0 = src[0], a1 = src[1], a2 = src[2], a3 = src[3];
+        const uint32_t w[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+        unpack_f32(w, sm, z);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    }
+    if (p.rht) fwht128_group(z, lig);
+    quant_block<MODE>(z, gb, active, p, s_t, lmax);
+  }
+  if constexpr (MODE == kAmax || MODE == kEden) {
+    const float m = block_max(lmax, red, kThreads);
+    if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
+  }
+}
+
+// ---------------------------------------------------------------- axis 1
+// Tile: TT = 256 positions along the reduction (input rows) x TC columns,
+// TC * sizeof(elem) = 128 bytes.  LDS holds the tile transposed: column c's
+// 256 values are contiguous (plus a 16-byte pad).
+template <int IN_BF16>
+struct ColTile {
+  static constexpr int TT = 256;
+  static constexpr int TC = IN_BF16 ? 64 : 32;
+  static constexpr int PITCH = TT + (IN_BF16 ? 8 : 4);  // elements
+  using elem = typename std::conditional<IN_BF16 != 0, uint16_t, float>::type;
+};
+
+template <int IN_BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
+  using CT = ColTile<IN_BF16>;
+  using elem = typename CT::elem;
+  constexpr int TT = CT::TT, TC = CT::TC, PITCH = CT::PITCH;
+  __shared__ __attribute__((aligned(16))) elem tile[TC * PITCH];
+  __shared__ float red[kThreads / kWave];
+
+  float s_t = 1.0f;
+  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kEdenFused) {
+    s_t = tensor_scale(p, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  }
+  const uint32_t lig = threadIdx.x & 7u;
+  const SignMasks sm = make_masks<IN_BF16>(p, lig);
+  const uint32_t nct = p.ctiles_div.d;
+  float lmax = 0.0f;
+
+  for (uint32_t t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
+    const uint32_t tt = fdiv(t, p.ctiles_div);
+    const uint32_t tc = t - tt * nct;
+    const uint32_t T0 = tt * TT, C0 = tc * TC;
+    __syncthreads();  // the previous tile's LDS reads are done
+    if (IN_BF16) {
+      // row pairs (2rp, 2rp+1) x 8 chunks of 8 columns; each thread packs
+      // the two rows of a column into one LDS word (even row in the low half).
+      const uint16_t *x = static_cast<const uint16_t *>(p.x);
+      uint32_t *tw = reinterpret_cast<uint32_t *>(tile);
+      for (uint32_t c = threadIdx.x; c < (TT / 2) * 8; c += kThreads) {
+        const uint32_t rp = c >> 3, q = c & 7u;
+        const uint32_t r0 = T0 + 2 * rp, col0 = C0 + 8 * q;
+        uint16_t v0[8], v1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v0[j] = v1[j] = 0;
+        if (col0 < p.cols) {
+          const bool full = p.vec && col0 + 8 <= p.cols;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t r = r0 + h;
+            if (r < p.rows) {
+              const uint16_t *src = x + (size_t)r * p.ld + col0;
+              uint16_t *dst = h ? v1 : v0;
+              if (full) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(src);
+                const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  dst[2 * j] = (uint16_t)(w[j] & 0xFFFFu);
+                  dst[2 * j + 1] = (uint16_t)(w[j] >> 16);
+                }
+              } else {
+                for (uint32_t j = 0; j < 8 && col0 + j < p.cols; ++j) dst[j] = src[j];
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          tw[((8 * q + j) * PITCH + 2 * rp) / 2] = (uint32_t)v0[j] | ((uint32_t)v1[j] << 16);
+      }
+    } else {
+      const float *x = static_cast<const float *>(p.x);
+      for (uint32_t c = threadIdx.x; c < TT * 8; c += kThreads) {
+        const uint32_t r = c >> 3, q = c & 7u;
+        const uint32_t row = T0 + r, col0 = C0 + 4 * q;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (row < p.rows && col0 < p.cols) {
+          const float *src = x + (size_t)row * p.ld + col0;
+          if (p.vec && col0 + 4 <= p.cols) {
+            const float4 a = *reinterpret_cast<const float4 *>(src);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+          } else {
+            for (uint32_t j = 0; j < 4 && col0 + j < p.cols; ++j) v[j] = src[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tile[(4 * q + j) * PITCH + r] = v[j];
+      }
+    }
+    __syncthreads();
+
+    // TC columns x 16 blocks each; a group of 8 lanes = 128 positions of one
+    // column; consecutive groups are the two halves of a column.
+    for (int round = 0; round < TC * (TT / 16) / kThreads; ++round) {
+      const uint32_t u = round * kThreads + threadIdx.x;
+      const uint32_t g = u >> 3;
+      const uint32_t c = g >> 1, h = g & 1u;
+      const uint32_t tb = h * 8 + lig;
+      const uint32_t col = C0 + c, kblk = T0 / 16 + tb;
+      const bool active = col < p.cols && kblk < p.K16;
+      float z[16];
+      if (IN_BF16) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(tile + c * PITCH + tb * 16);
+        const uint4 a0 = src[0], a1 = src[1];
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        unpack_bf16(w, sm, z);
+      } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(tile + c * PITCH + tb * 16);
+        const uint4 a0 = src[0], a1 = src[1], a2 = src[2], a3 = src[3];
+        const uint32_t w[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+        unpack_f32(w, sm, z);
+      }
+      if (p.rht) fwht128_group(z, lig);
+      const uint32_t gb = col * p.K16 + kblk;
+      quant_block<MODE>(z, active ? gb : 0u, active, p, s_t, lmax);
+    }
+  }
+  if constexpr (MODE == kAmax || MODE == kEden) {
+    const float m = block_max(lmax, red, kThreads);
+    if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
+  }
+}
+
+// ---------------------------------------------------------------- MS-EDEN scales
+// s_t = max t / 448 (or the given scale); scale = SR of min(t / s_t, 448)
+// onto the E4M3 grid, one Philox call per 8 consecutive blocks (tag 1).
+__global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
+  __shared__ float red[kThreads / kWave];
+  float s_t;
+  if (p.ts_in) {
+    s_t = *p.ts_in;
+  } else {
+    float m = 0.0f;
+    for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.partial[i]);
+    m = block_max(m, red, kThreads);
+    s_t = (m > 0.0f) ? m / 448.0f : 1.0f;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  const uint32_t ncalls = (p.nblocks + 7u) / 8u;
+  for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < ncalls; c += gridDim.x * kThreads) {
+    const Philox4 u = uniforms8(p.key, (uint64_t)c, 1u);
+    const uint32_t b0 = c * 8u;
+    if (b0 + 8u <= p.nblocks) {
+      const float4 t0 = *reinterpret_cast<const float4 *>(p.tb + b0);
+      const float4 t1 = *reinterpret_cast<const float4 *>(p.tb + b0 + 4);
+      const float t[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = e4m3_sr_sat(fminf(t[j] / s_t, 448.0f), uniform_at(u, j));
+        if (j < 4) lo |= e << (8 * j);
+        else hi |= e << (8 * (j - 4));
+      }
+      *reinterpret_cast<uint2 *>(p.scales + b0) = make_uint2(lo, hi);
+    } else {
+      for (uint32_t j = 0; b0 + j < p.nblocks; ++j)
+        p.scales[b0 + j] = (uint8_t)e4m3_sr_sat(fminf(p.tb[b0 + j] / s_t, 448.0f), uniform_at(u, (int)j));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+uint32_t quant_grid(const QuantParams &p, int in_bf16, int axis) {
+  (void)in_bf16;
+  uint64_t units = axis == 0 ? ((uint64_t)p.nblocks + kThreads - 1) / kThreads : p.ntiles;
+  if (units < 1) units = 1;
+  return (uint32_t)(units < (uint64_t)kMaxPartials ? units : kMaxPartials);
+}
+
+uint32_t eden_scales_grid(const QuantParams &p) {
+  uint64_t calls = ((uint64_t)p.nblocks + 7) / 8;
+  uint64_t g = (calls + kThreads - 1) / kThreads;
+  if (g < 1) g = 1;
+  return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);
+}
+
+template <int IN_BF16, int MODE>
+static void launch_one(const QuantParams &p, int axis, uint32_t grid, hipStream_t s) {
+  if (axis == 0)
+    hipLaunchKernelGGL((k_quant_rows<IN_BF16, MODE>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_quant_cols<IN_BF16, MODE>), dim3(grid), dim3(kThreads), 0, s, p);
+}
+
+template <int IN_BF16>
+static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid, hipStream_t s) {
+  switch (mode) {
+    case kAmax: launch_one<IN_BF16, kAmax>(p, axis, grid, s); break;
+    case kRtn: launch_one<IN_BF16, kRtn>(p, axis, grid, s); break;
+    case kSr: launch_one<IN_BF16, kSr>(p, axis, grid, s); break;
+    case kIf4: launch_one<IN_BF16, kIf4>(p, axis, grid, s); break;
+    case kEden: launch_one<IN_BF16, kEden>(p, axis, grid, s); break;
+    case kEdenFused: launch_one<IN_BF16, kEdenFused>(p, axis, grid, s); break;
+    case kRot: launch_one<IN_BF16, kRot>(p, axis, grid, s); break;
+  }
+}
+
+hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, uint32_t grid,
+                        hipStream_t s) {
+  if (in_bf16)
+    launch_mode<1>(p, axis, mode, grid, s);
+  else
+    launch_mode<0>(p, axis, mode, grid, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_eden_scales(const QuantParams &p, uint32_t grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_eden_scales, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace nv4

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before enqueuing anything (the checks are host-side; no call here reaches a
+launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP_ERR, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+FAKE = 0x7f0000000000   # 256-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_bit_block_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from nvfp4_bit_block_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(nvfp4_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_functions_exported(nv):
+    names = declared_functions()
+    assert len(names) >= 10
+    L = nv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(nv):
+    L = nv.lib()
+    assert nv.abi_version() == 1
+    for st, text in ((OK, b"ok"), (INVALID, b"invalid argument"), (SHAPE, b"bad shape"),
+                     (MISALIGNED, b"misaligned pointer or stride"), (WS_SMALL, b"workspace too small"),
+                     (HIP_ERR, b"HIP error"), (UNSUPPORTED, b"unsupported")):
+        assert L.nvfp4_status_string(st) == text
+
+
+def _opts(nv, **kw):
+    o = nv._Opts()
+    nv.lib().nvfp4_opts_init(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def _q(nv, rows=64, cols=256, ld=None, dtype=1, x=FAKE, codes=FAKE, scales=FAKE, ts=FAKE, ws=FAKE,
+       ws_bytes=1 << 30, fn="nvfp4_quantize_nvfp4", **kw):
+    o = _opts(nv, **kw)
+    f = getattr(nv.lib(), fn)
+    return f(ctypes.c_void_p(x), dtype, rows, cols, cols if ld is None else ld, ctypes.byref(o),
+             ctypes.c_void_p(codes), ctypes.c_void_p(scales), ctypes.c_void_p(ts), ctypes.c_void_p(ws),
+             ws_bytes, None)
+
+
+def test_workspace_size(nv):
+    L = nv.lib()
+    o = _opts(nv)
+    assert L.nvfp4_workspace_size(64, 256, ctypes.byref(o)) == 16384
+    o = _opts(nv, rounding=2)
+    assert L.nvfp4_workspace_size(64, 256, ctypes.byref(o)) == 16384 + 64 * 16 * 4
+    o = _opts(nv, rounding=2, axis=1)
+    assert L.nvfp4_workspace_size(256, 64, ctypes.byref(o)) == 16384 + 64 * 16 * 4
+    assert L.nvfp4_workspace_size(-1, 4, ctypes.byref(o)) == 0
+
+
+def test_quantize_rejections(nv):
+    L = nv.lib()
+    assert _q(nv, cols=100) == SHAPE                      # K % 16
+    assert _q(nv, cols=144, rht=1) == SHAPE               # K % 128 with rotation
+    assert _q(nv, cols=144, rounding=2) == SHAPE          # MS-EDEN group 128
+    assert _q(nv, rows=144, cols=64, axis=1, rht=1) == SHAPE   # axis 1: K = rows
+    assert _q(nv, rows=100, cols=64, axis=1) == SHAPE     # axis 1: K = rows
+    assert _q(nv, rounding=7) == INVALID
+    assert _q(nv, axis=2) == INVALID
+    assert _q(nv, rht=3) == INVALID
+    assert _q(nv, rounding=2, eden_group=32) == INVALID
+    assert _q(nv, dtype=5) == INVALID
+    assert _q(nv, rows=-1) == INVALID
+    assert _q(nv, ld=128) == SHAPE                        # ld < cols
+    assert _q(nv, x=0) == INVALID
+    assert _q(nv, codes=0) == INVALID
+    assert _q(nv, ts=0) == INVALID
+    assert _q(nv, x=FAKE + 8) == MISALIGNED
+    assert _q(nv, ld=260, dtype=1) == MISALIGNED          # 520-byte rows
+    assert _q(nv, codes=FAKE + 4) == MISALIGNED
+    assert _q(nv, ws=FAKE + 16) == MISALIGNED
+    assert _q(nv, ws_bytes=100) == WS_SMALL
+    assert _q(nv, fn="nvfp4_quantize_if4", rounding=1) == INVALID
+    _q(nv, cols=100)
+    assert b"multiple of 16" in L.nvfp4_last_error()
+
+
+def test_dequantize_and_gemm_rejections(nv):
+    L = nv.lib()
+    P = ctypes.c_void_p
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 4, 100, 0, None, 0, P(FAKE), None) == SHAPE
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 4, 64, 3, None, 0, P(FAKE), None) == INVALID
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 4, 64, 0, None, 9, P(FAKE), None) == INVALID
+    w = (ctypes.c_uint32 * 4)()
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 4, 64, 0, w, 0, P(FAKE), None) == SHAPE
+    assert L.nvfp4_dequantize(P(0), P(FAKE), P(FAKE), 4, 64, 0, None, 0, P(FAKE), None) == INVALID
+    assert L.nvfp4_dequantize(P(FAKE + 2), P(FAKE), P(FAKE), 4, 64, 0, None, 0, P(FAKE), None) == MISALIGNED
+    assert L.nvfp4_dequantize(P(0), P(0), P(0), 0, 64, 0, None, 0, P(0), None) == OK   # empty
+    g = L.nvfp4_gemm_nvfp4
+    assert g(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 40, P(FAKE), 0, 8, None) == SHAPE
+    assert g(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 64, P(FAKE), 0, 4, None) == SHAPE
+    assert g(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 64, P(FAKE), 3, 8, None) == INVALID
+    assert g(P(FAKE), P(FAKE), P(FAKE), P(0), P(FAKE), P(FAKE), 8, 8, 64, P(FAKE), 0, 8, None) == INVALID
+    assert g(P(FAKE + 4), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 64, P(FAKE), 0, 8, None) == MISALIGNED
+    assert g(P(0), P(0), P(0), P(0), P(0), P(0), 0, 8, 64, P(0), 0, 8, None) == OK      # empty
+    assert L.nvfp4_rht(P(FAKE), 1, 4, 100, 100, 0, w, P(FAKE), None) == SHAPE
+    assert L.nvfp4_rht(P(FAKE), 1, 4, 128, 128, 0, None, P(FAKE), None) == INVALID

@@ -1,0 +1,78 @@
+"""GPU block-scaled FP4 GEMM against the oracle's fp64 GEMM on the same
+packed operands (quantized by the oracle, uploaded).  Bar: relative Frobenius
+error <= 1e-3 with fp32 output; the dequantized products are exact in fp16,
+so the only error is fp32 accumulation order."""
+import numpy as np
+import pytest
+
+import oracle
+from nvfp4_bit_block_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_bit_block_amd as m
+    m.lib()
+    return m
+
+
+def upload(nv, ref):
+    import torch
+    return nv.QTensor(torch.from_numpy(ref["codes"]).to("cuda:0"),
+                      torch.from_numpy(ref["scales"]).to("cuda:0"),
+                      torch.tensor([ref["ts"]], dtype=torch.float32, device="cuda:0"), nv.FORMAT_NVFP4)
+
+
+def rel_fro(got, ref):
+    return float(np.linalg.norm(got.astype(np.float64) - ref) / np.linalg.norm(ref))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 528), (1, 17, 64), (513, 259, 1024),
+                                   (64, 640, 2064), (768, 512, 4096)])
+def test_gemm_small_shapes(nv, M, N, K):
+    import torch
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = oracle.quantize(rng.standard_normal((M, K)).astype(np.float32))
+    b = oracle.quantize((0.02 * rng.standard_normal((N, K))).astype(np.float32), rounding=oracle.SR, seed=1)
+    ref = oracle.gemm_full(a, b)
+    c = nv.gemm_nvfp4(upload(nv, a), upload(nv, b)).cpu().numpy()
+    assert c.shape == (M, N)
+    assert rel_fro(c, ref) <= 1e-3
+    assert rel_fro(c, ref) <= 1e-5   # in practice: fp32 accumulation only
+    c16 = nv.gemm_nvfp4(upload(nv, a), upload(nv, b), out_dtype=torch.bfloat16).float().cpu().numpy()
+    # bf16 output: the fp32 result rounded once more (2^-9 relative) plus accumulation noise
+    assert np.all(np.abs(c16 - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+def test_gemm_ldc_and_strided_output(nv):
+    import torch
+    rng = np.random.default_rng(5)
+    a = oracle.quantize(rng.standard_normal((130, 256)).astype(np.float32))
+    b = oracle.quantize(rng.standard_normal((70, 256)).astype(np.float32))
+    ref = oracle.gemm_full(a, b)
+    big = torch.full((130, 96), -7.0, dtype=torch.float32, device="cuda:0")
+    out = big[:, 10:80]
+    nv.gemm_nvfp4(upload(nv, a), upload(nv, b), out=out)
+    h = big.cpu().numpy()
+    assert rel_fro(h[:, 10:80], ref) <= 1e-5
+    assert np.all(h[:, :10] == -7.0) and np.all(h[:, 80:] == -7.0)
+
+
+def test_gemm_rotated_operands_match_unrotated_product(nv):
+    """With the same signs on both operands, (H D a) . (H D b) = a . b: the
+    GEMM of rotated, MS-EDEN-quantized operands estimates A B^T."""
+    rng = np.random.default_rng(6)
+    signs = synth.signs_from_rng(rng)
+    w = oracle.signs_words(signs)
+    A = rng.standard_normal((128, 1024)).astype(np.float32)
+    B = rng.standard_normal((96, 1024)).astype(np.float32)
+    qa = oracle.quantize(A, rounding=oracle.MSEDEN, rht_on=True, signs_w=w, seed=1)
+    qb = oracle.quantize(B, rounding=oracle.MSEDEN, rht_on=True, signs_w=w, seed=2)
+    c = nv.gemm_nvfp4(upload(nv, qa), upload(nv, qb)).cpu().numpy()
+    ref = A.astype(np.float64) @ B.T.astype(np.float64)
+    assert rel_fro(c, oracle.gemm_full(qa, qb)) <= 1e-5
+    assert rel_fro(c, ref) < 0.2     # a 4-bit estimate of the exact product

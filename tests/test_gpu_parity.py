@@ -1,0 +1,195 @@
+"""GPU <-> oracle parity of the quantizers, the rotation and dequantization,
+called through the C ABI (the Python binding marshals arguments only).
+
+Rotation off: packed codes, scales and the tensor scale are bit-exact.
+Rotation on: the kernels run the transform's stages in the oracle's order, so
+they are bit-exact too in practice; the assertion is the contract's
+(<= 1e-5 of codes one level apart, rotated values within 1e-5 relative).
+Sizes span several workgroups and a ragged tail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from nvfp4_bit_block_amd import synth
+from gpu_util import assert_bit_exact, assert_rotated_close, q_to_host, to_device
+
+pytestmark = pytest.mark.gpu
+
+ROUNDINGS = [("rtn", oracle.RTN, 128), ("sr", oracle.SR, 128), ("eden128", oracle.MSEDEN, 128),
+             ("eden16", oracle.MSEDEN, 16)]
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nvfp4_bit_block_amd as m
+    m.lib()
+    return m
+
+
+def _run(nv, x, dtype, rnd, axis, signs, seed=11, stream=5, group=128, if4=False):
+    xt = to_device(x, dtype)
+    if if4:
+        q = nv.quantize_if4(xt, axis=axis, rht_signs=signs)
+    else:
+        q = nv.quantize_nvfp4(xt, rounding=rnd, axis=axis, rht_signs=signs, seed=seed,
+                              stream_id=stream, eden_group=group)
+    return q_to_host(q)
+
+
+def _ref(x, rnd, axis, signs, seed=11, stream=5, group=128, fmt=oracle.FMT_NVFP4):
+    w = None if signs is None else oracle.signs_words(signs)
+    return oracle.quantize(x, fmt=fmt, rounding=rnd, axis=axis, rht_on=signs is not None,
+                           signs_w=w, seed=seed, stream=stream, eden_group=group)
+
+
+# shapes (rows, cols): quantized dim must be a multiple of 128 for rotation and
+# MS-EDEN-128, of 16 otherwise; several workgroups plus ragged tails.
+ROW_SHAPES = [(256, 256), (37, 1152), (1, 128), (300, 384)]
+COL_SHAPES = [(256, 256), (1152, 37), (128, 1), (512, 200), (384, 72)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("name,rnd,group", ROUNDINGS)
+@pytest.mark.parametrize("axis", [0, 1])
+def test_quantize_bit_exact_rotation_off(nv, dtype, name, rnd, group, axis):
+    shapes = ROW_SHAPES if axis == 0 else COL_SHAPES
+    for i, (r, c) in enumerate(shapes):
+        x = synth.gradient(r, c, seed=100 + i)[0] if dtype == "bf16" else synth.gaussian(r, c, seed=100 + i)
+        g = _run(nv, x, dtype, rnd, axis, None, group=group)
+        ref = _ref(x, rnd, axis, None, group=group)
+        assert_bit_exact(g, ref, f"{name} {dtype} axis{axis} {r}x{c}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("name,rnd,group", ROUNDINGS)
+@pytest.mark.parametrize("axis", [0, 1])
+def test_quantize_rotation_on(nv, dtype, name, rnd, group, axis):
+    rng = np.random.default_rng(7)
+    signs = synth.signs_from_rng(rng)
+    shapes = [(256, 256), (40, 1024)] if axis == 0 else [(256, 256), (1024, 40), (384, 72)]
+    for i, (r, c) in enumerate(shapes):
+        x = synth.gradient(r, c, seed=200 + i)[0] if dtype == "bf16" else synth.gaussian(r, c, seed=200 + i)
+        g = _run(nv, x, dtype, rnd, axis, signs, group=group)
+        ref = _ref(x, rnd, axis, signs, group=group)
+        assert_rotated_close(g, ref, what=f"{name} {dtype} axis{axis} {r}x{c}")
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_if4_bit_exact(nv, axis, dtype):
+    for i, (r, c) in enumerate([(256, 256), (64, 1040), (1040, 64)] if axis == 0 else
+                               [(256, 256), (1040, 64), (64, 1040)]):
+        x = synth.weight(r, c, seed=300 + i)
+        if dtype == "fp32":
+            x = synth.gaussian(r, c, seed=300 + i) * np.float32(3.0)
+        g = _run(nv, x, dtype, oracle.RTN, axis, None, if4=True)
+        ref = _ref(x, oracle.RTN, axis, None, fmt=oracle.FMT_IF4)
+        assert_bit_exact(g, ref, f"if4 {dtype} axis{axis} {r}x{c}")
+        assert np.any(g["scales"] >= 0x80) and np.any(g["scales"] < 0x80)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_rht_values(nv, axis):
+    import torch
+    rng = np.random.default_rng(8)
+    signs = synth.signs_from_rng(rng)
+    x = synth.gradient(256, 384, seed=9)[0]
+    z = nv.rht(to_device(x, "bf16"), signs, axis=axis).cpu().numpy()
+    view = x if axis == 0 else np.ascontiguousarray(x.T)
+    ref = oracle.rht(view, oracle.signs_words(signs))
+    rel = np.abs(z - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert np.max(np.abs(z - ref) / (np.abs(ref).max())) <= 1e-5
+    assert np.mean(rel > 1e-5) <= 1e-5
+    torch.cuda.synchronize()
+
+
+def test_tensor_scale_in(nv):
+    import torch
+    x = synth.gaussian(128, 512, seed=12)
+    ts = torch.tensor([0.0123], dtype=torch.float32, device="cuda:0")
+    for rnd in (oracle.RTN, oracle.SR, oracle.MSEDEN):
+        q = q_to_host(nv.quantize_nvfp4(to_device(x, "fp32"), rounding=rnd, seed=3, stream_id=1,
+                                        tensor_scale_in=ts))
+        ref = oracle.quantize(x, rounding=rnd, seed=3, stream=1, ts_in=np.float32(0.0123))
+        assert_bit_exact(q, ref, f"ts_in rounding {rnd}")
+
+
+def upload(nv, ref, fmt):
+    """A QTensor on the device holding the oracle's packed output."""
+    import torch
+    return nv.QTensor(torch.from_numpy(ref["codes"]).to("cuda:0"),
+                      torch.from_numpy(ref["scales"]).to("cuda:0"),
+                      torch.tensor([ref["ts"]], dtype=torch.float32, device="cuda:0"), fmt)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "if4"])
+def test_dequantize_bit_exact(nv, fmt):
+    import torch
+    x = synth.weight(96, 512, seed=13)
+    ofmt = oracle.FMT_IF4 if fmt == "if4" else oracle.FMT_NVFP4
+    q = oracle.quantize(x, fmt=ofmt) if fmt == "if4" else oracle.quantize(x, rounding=oracle.SR, seed=4)
+    ref = oracle.dequantize(q["codes"], q["scales"], q["ts"], fmt=ofmt)
+    qt = upload(nv, q, nv.FORMAT_IF4 if fmt == "if4" else nv.FORMAT_NVFP4)
+    d = nv.dequantize(qt).cpu().numpy()
+    assert np.array_equal(d.view(np.uint32), ref.view(np.uint32))
+    d16 = nv.dequantize(qt, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(d16, synth.to_bf16_f32(ref))
+
+
+def test_dequantize_inverse_rotation(nv):
+    rng = np.random.default_rng(14)
+    signs = synth.signs_from_rng(rng)
+    w = oracle.signs_words(signs)
+    x = synth.gradient(64, 1024, seed=15)[0]
+    q = oracle.quantize(x, rounding=oracle.MSEDEN, rht_on=True, signs_w=w, seed=1)
+    ref = oracle.dequantize(q["codes"], q["scales"], q["ts"], inv_signs_w=w)
+    d = nv.dequantize(upload(nv, q, nv.FORMAT_NVFP4), inv_rht_signs=signs).cpu().numpy()
+    assert np.max(np.abs(d - ref)) <= 1e-5 * np.abs(ref).max()
+
+
+def test_deterministic_replay(nv):
+    x = synth.gradient(512, 1024, seed=16)[0]
+    xt = to_device(x, "bf16")
+    signs = synth.signs_from_rng(np.random.default_rng(3))
+    a = q_to_host(nv.quantize_nvfp4(xt, rounding="sr", rht_signs=signs, seed=9, stream_id=2))
+    b = q_to_host(nv.quantize_nvfp4(xt, rounding="sr", rht_signs=signs, seed=9, stream_id=2))
+    assert_bit_exact(a, b, "replay")
+    c = q_to_host(nv.quantize_nvfp4(xt, rounding="sr", rht_signs=signs, seed=9, stream_id=3))
+    assert not np.array_equal(a["codes"], c["codes"])
+
+
+def test_strided_input(nv):
+    """A row-major view with leading dimension above the row length."""
+    import torch
+    x = synth.gaussian(64, 320, seed=17)
+    full = torch.from_numpy(x).to("cuda:0")
+    view = full[:, 32:288]
+    assert view.stride(0) == 320
+    for axis in (0, 1):
+        g = q_to_host(nv.quantize_nvfp4(view, rounding="rtn", axis=axis))
+        ref = oracle.quantize(np.ascontiguousarray(x[:, 32:288]), axis=axis)
+        assert_bit_exact(g, ref, f"strided axis{axis}")
+
+
+def test_zero_tensor_and_empty(nv):
+    import torch
+    z = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda:0")
+    for rnd in ("rtn", "sr", "mseden"):
+        h = q_to_host(nv.quantize_nvfp4(z, rounding=rnd))
+        assert h["ts"] == 1.0 and not h["scales"].any() and not h["codes"].any()
+    e = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda:0")
+    h = q_to_host(nv.quantize_nvfp4(e))
+    assert h["ts"] == 1.0 and h["codes"].size == 0
+
+
+def test_negative_zero_sign_kept(nv):
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, :8] = -0.0
+    x[0, 8] = 1.0
+    x[0, 9] = -1e-6
+    g = _run(nv, x, "fp32", oracle.RTN, 0, None)
+    ref = _ref(x, oracle.RTN, 0, None)
+    assert_bit_exact(g, ref, "signed zeros")
