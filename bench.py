@@ -1,0 +1,312 @@
+"""Benchmark: one quantized training step of an MLP up-projection on one
+MI355X, through the library's C ABI.
+
+Step (Quartet II linear-layer scheme: forward RTN NVFP4, backward
+re-quantization along the reduction dimension with the randomized Hadamard
+rotation and MS-EDEN):
+  forward   qX  = RTN(X)            [32768 x 4096]   axis 0
+            qW  = RTN(W)            [11008 x 4096]   axis 0
+            Y   = qX qW^T           [32768 x 11008]  bf16
+  backward  qdYr = MSEDEN(dY)       [32768 x 11008]  axis 0, rotation
+            qWc  = MSEDEN(W)        [4096 x 11008]   axis 1, rotation
+            dX   = qdYr qWc^T       [32768 x 4096]   bf16
+            qdYc = MSEDEN(dY)       [11008 x 32768]  axis 1, rotation
+            qXc  = MSEDEN(X)        [4096 x 32768]   axis 1, rotation
+            dW   = qdYc qXc^T       [11008 x 4096]   fp32
+Inputs: X ~ N(0,1), W ~ N(0, 0.02^2), dY ~ N(0, 1e-3^2), bf16, seed 4.
+
+Reported: `value` = quantizer throughput over the six quantizations, in
+algorithmic GB/s (bf16 input read once + codes + scales written once =
+2.5625 bytes per element) divided by their measured time; `gemm` = the three
+GEMMs' 2MNK flops over their time.  `roofline` describes the GEMM kernel
+(the dominant one), `cpu_baseline` the CPU oracle on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 quantize GB/s (% HBM peak); block-scaled FP4 GEMM TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+BYTES_PER_ELEM_BF16 = 2.5625   # 2 (read) + 0.5 (codes) + 0.0625 (scales)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate budget for the CPU oracle sample")
+    return ap.parse_args()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "nvfp4_bit_block_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, digest, launch_flops_or_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the quantizers and the "
+                          "GEMM are single-device kernels; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+    import torch
+    import nvfp4_bit_block_amd as nv
+    from nvfp4_bit_block_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nv.lib()
+
+    T, D, O = synth.MLP_SHAPES["X"][0], synth.MLP_SHAPES["X"][1], synth.MLP_SHAPES["W"][0]
+    t0 = time.time()
+    rng = np.random.default_rng(4)
+
+    def draw(shape, scale):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        if scale != 1.0:
+            a *= np.float32(scale)
+        g = torch.from_numpy(a).to(dev).to(torch.bfloat16)   # round to nearest even
+        return a, g
+
+    Xh, X = draw((T, D), 1.0)
+    Wh, W = draw((O, D), 0.02)
+    dYh, dY = draw((T, O), 1e-3)
+    signs = synth.signs_from_rng(rng)
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def ws_for(rows, cols, rounding, axis):
+        return torch.empty(nv.workspace_size(rows, cols, rounding, axis), dtype=torch.uint8, device=dev)
+
+    def qt(rows_out, k):
+        return nv.QTensor(torch.empty((rows_out, k // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((rows_out, k // 16), dtype=torch.uint8, device=dev),
+                          torch.empty(1, dtype=torch.float32, device=dev))
+
+    # preallocated outputs and workspaces: the timed region allocates nothing
+    plan = [  # name, input, rounding, axis, rotation, rows_out, K
+        ("qX", X, nv.RTN, 0, None, T, D),
+        ("qW", W, nv.RTN, 0, None, O, D),
+        ("qdYr", dY, nv.MSEDEN, 0, signs, T, O),
+        ("qWc", W, nv.MSEDEN, 1, signs, D, O),
+        ("qdYc", dY, nv.MSEDEN, 1, signs, O, T),
+        ("qXc", X, nv.MSEDEN, 1, signs, D, T),
+    ]
+    outs = {n: qt(r, k) for n, _, _, _, _, r, k in plan}
+    wss = {n: ws_for(x.shape[0], x.shape[1], rnd, ax) for n, x, rnd, ax, _, _, _ in plan}
+    Y = torch.empty((T, O), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((O, D), dtype=torch.float32, device=dev)
+    gemms = [("Y", "qX", "qW", Y), ("dX", "qdYr", "qWc", dX), ("dW", "qdYc", "qXc", dW)]
+    stream = torch.cuda.current_stream()
+
+    def quantize(name, x, rnd, ax, sg, step):
+        nv.quantize_nvfp4(x, rounding=rnd, axis=ax, rht_signs=sg, seed=1000 + len(name), stream_id=step,
+                          out=outs[name], workspace=wss[name])
+
+    ev_pool = []
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev_pool.append(e)
+        return e
+
+    def step(i, timed):
+        marks = []
+        for n, x, rnd, ax, sg, _, _ in plan[:2]:
+            a = ev() if timed else None
+            quantize(n, x, rnd, ax, sg, i)
+            marks.append(("q", n, a, ev() if timed else None))
+        a = ev() if timed else None
+        nv.gemm_nvfp4(outs["qX"], outs["qW"], out=Y)
+        marks.append(("g", "Y", a, ev() if timed else None))
+        for n, x, rnd, ax, sg, _, _ in plan[2:4]:
+            a = ev() if timed else None
+            quantize(n, x, rnd, ax, sg, i)
+            marks.append(("q", n, a, ev() if timed else None))
+        a = ev() if timed else None
+        nv.gemm_nvfp4(outs["qdYr"], outs["qWc"], out=dX)
+        marks.append(("g", "dX", a, ev() if timed else None))
+        for n, x, rnd, ax, sg, _, _ in plan[4:6]:
+            a = ev() if timed else None
+            quantize(n, x, rnd, ax, sg, i)
+            marks.append(("q", n, a, ev() if timed else None))
+        a = ev() if timed else None
+        nv.gemm_nvfp4(outs["qdYc"], outs["qXc"], out=dW)
+        marks.append(("g", "dW", a, ev() if timed else None))
+        return marks
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    all_marks = []
+    start.record(stream)
+    for i in range(args.steps):
+        all_marks.append(step(args.warmup + i, True))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    qms = {n: 0.0 for n, *_ in plan}
+    gms = {n: 0.0 for n, *_ in gemms}
+    for marks in all_marks:
+        for kind, n, a, b in marks:
+            (qms if kind == "q" else gms)[n] += a.elapsed_time(b)
+    for d in (qms, gms):
+        for n in d:
+            d[n] /= args.steps
+    q_elems = {n: x.numel() for n, x, *_ in plan}
+    q_bytes = sum(q_elems[n] * BYTES_PER_ELEM_BF16 for n in q_elems)
+    q_time_ms = sum(qms.values())
+    q_gbs = q_bytes / (q_time_ms * 1e-3) / 1e9
+    flops = {"Y": 2.0 * T * O * D, "dX": 2.0 * T * D * O, "dW": 2.0 * O * D * T}
+    g_time_ms = sum(gms.values())
+    g_tflops = sum(flops.values()) / (g_time_ms * 1e-3) / 1e12
+    gemm_launch_ms = g_time_ms / 3.0
+    gemm_flops_launch = flops["Y"]
+    achieved = gemm_flops_launch / (gemm_launch_ms * 1e-3) / 1e12
+
+    kernels = {}
+    for n, x, rnd, ax, sg, r, k in plan:
+        gbs = q_elems[n] * BYTES_PER_ELEM_BF16 / (qms[n] * 1e-3) / 1e9
+        kernels[n] = {"ms": round(qms[n], 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                      "rounding": ["rtn", "sr", "mseden"][rnd], "axis": ax, "rotation": sg is not None,
+                      "shape_in": list(x.shape)}
+    for n, *_ in gemms:
+        tf = flops[n] / (gms[n] * 1e-3) / 1e12
+        kernels["gemm_" + n] = {"ms": round(gms[n], 4), "TFLOP/s": round(tf, 1),
+                                "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 3)}
+
+    digest = source_digest("gemm.hip", "common.hpp", "kernels.hpp")
+    traffic = measured_traffic("k_gemm", digest, gemm_flops_launch)
+    result = {
+        "metric": METRIC,
+        "value": round(q_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mlp_up_projection_training_step", "X": [T, D], "W": [O, D],
+                   "dY": [T, O], "input_dtype": "bf16", "rotation": 128,
+                   "quantizations": "RTN(X,W) fwd; RHT+MS-EDEN(dY row+col, W col, X col) bwd",
+                   "gemms": "Y=XW^T (bf16), dX=dY W (bf16), dW=dY^T X (fp32)"},
+        "hbm_frac": round(q_gbs / HBM_PEAK_GBS, 3),
+        "gemm": {"value": round(g_tflops, 1), "unit": "TFLOP/s",
+                 "frac": round(g_tflops / MFMA_F16_PEAK_TFLOPS, 3),
+                 "dtype": "f16 MFMA on exactly dequantized FP4, f32 accumulate"},
+        "roofline": {"kernel": "k_gemm", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "launch_ms": round(gemm_launch_ms, 4),
+                     "flops_per_launch": gemm_flops_launch},
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(Xh, Wh, dYh, signs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(Xh, Wh, dYh, signs, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same step:
+    the same six quantizations restricted to slices of the inputs (each
+    slice quantized as its own tensor), and sampled dW outputs computed one
+    by one.  A small calibration pass sizes the slices so that the measured
+    pass takes about `budget_s` seconds."""
+    import oracle
+    from nvfp4_bit_block_amd import synth
+    w = oracle.signs_words(signs)
+    T, D = Xh.shape
+    O = Wh.shape[0]
+
+    def jobs(rows):
+        """(label, array, rounding, axis, rotation) for a slice of `rows` rows
+        of the token dimension (and proportionally of W)."""
+        ro = max(128, min(O, rows * O // T) // 128 * 128)
+        cols = max(128, min(D, rows // 4) // 128 * 128)
+        return [
+            (f"X[:{rows}] RTN", Xh[:rows], oracle.RTN, 0, False),
+            (f"W[:{ro}] RTN", Wh[:ro], oracle.RTN, 0, False),
+            (f"dY[:{rows}] MS-EDEN+RHT rows", dYh[:rows], oracle.MSEDEN, 0, True),
+            (f"W[:, :{cols}] MS-EDEN+RHT cols", Wh[:, :cols], oracle.MSEDEN, 1, True),
+            (f"dY[:{rows}] MS-EDEN+RHT cols", dYh[:rows], oracle.MSEDEN, 1, True),
+            (f"X[:{rows}] MS-EDEN+RHT cols", Xh[:rows], oracle.MSEDEN, 1, True),
+        ]
+
+    def run(rows):
+        t_q, b_q = 0.0, 0.0
+        for _, x, rnd, axis, rot in jobs(rows):
+            xb = synth.to_bf16_f32(x)
+            t = time.perf_counter()
+            oracle.quantize(xb, rounding=rnd, axis=axis, rht_on=rot, signs_w=w if rot else None, seed=1)
+            t_q += time.perf_counter() - t
+            b_q += xb.size * BYTES_PER_ELEM_BF16
+        return t_q, b_q
+
+    t_start = time.perf_counter()
+    t_cal, _ = run(128)
+    rows = int(128 * max(1.0, 0.8 * budget_s / max(t_cal, 1e-3)))
+    rows = max(128, min(T, rows // 128 * 128))
+    t_q, b_q = run(rows)
+    labels = "; ".join(j[0] for j in jobs(rows))
+    # GEMM: sampled output entries of dW (K = T), one by one
+    qa = oracle.quantize(synth.to_bf16_f32(dYh[:, :64]), rounding=oracle.MSEDEN, axis=1, rht_on=True,
+                         signs_w=w)
+    qb = oracle.quantize(synth.to_bf16_f32(Xh[:, :64]), rounding=oracle.MSEDEN, axis=1, rht_on=True,
+                         signs_w=w)
+    rng = np.random.default_rng(0)
+    n_ent = 1024
+    im, in_ = rng.integers(0, 64, n_ent), rng.integers(0, 64, n_ent)
+    t = time.perf_counter()
+    oracle.gemm_entries(qa, qb, im, in_)
+    t_g = time.perf_counter() - t
+    return {"value": round(b_q / t_q / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"quantize {labels} (bf16 inputs, {b_q / 2.5625 / 1e6:.1f} M elements); "
+                      f"gemm: {n_ent} dW entries one by one (K={T})",
+            "gemm_TFLOP/s": round(n_ent * 2.0 * T / t_g / 1e12, 6),
+            "seconds": round(time.perf_counter() - t_start, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -76,3 +76,25 @@ def test_gemm_rotated_operands_match_unrotated_product(nv):
     ref = A.astype(np.float64) @ B.T.astype(np.float64)
     assert rel_fro(c, oracle.gemm_full(qa, qb)) <= 1e-5
     assert rel_fro(c, ref) < 0.2     # a 4-bit estimate of the exact product
+
+
+def test_gemm_subnormal_and_zero_scales(nv):
+    """Rows spanning 2^0 .. 2^-30 in magnitude under one tensor scale give
+    subnormal and zero E4M3 block scales; all-zero blocks give scale 0."""
+    rng = np.random.default_rng(7)
+    A = rng.standard_normal((96, 512)).astype(np.float32)
+    A *= (2.0 ** -(np.arange(96) % 31)).astype(np.float32)[:, None]
+    A[5, 32:64] = 0.0
+    B = rng.standard_normal((64, 512)).astype(np.float32)
+    B *= (2.0 ** -(np.arange(64) % 17)).astype(np.float32)[:, None]
+    qa, qb = oracle.quantize(A), oracle.quantize(B, rounding=oracle.SR, seed=3)
+    assert np.any((qa["scales"] > 0) & (qa["scales"] < 8))       # subnormal E4M3 scales
+    assert np.any(qa["scales"] == 0)
+    ref = oracle.gemm_full(qa, qb)
+    c = nv.gemm_nvfp4(upload(nv, qa), upload(nv, qb)).cpu().numpy()
+    assert rel_fro(c, ref) <= 1e-5
+    # row by row as well: tiny rows must not be swamped by large ones
+    for r in (0, 9, 20, 30, 60, 90):
+        nr = np.linalg.norm(ref[r])
+        if nr > 0:
+            assert np.linalg.norm(c[r] - ref[r]) <= 1e-5 * nr
