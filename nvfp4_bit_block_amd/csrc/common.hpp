@@ -30,6 +30,23 @@ __device__ __forceinline__ int ilog2_floor_clamped(float v, int lo) {
   return e < lo ? lo : e;
 }
 
+// ---------------------------------------------------------------- division
+// a / d for the constants d = 6 and 7, correctly rounded: q0 = a * fp32(1/d),
+// r = fma(-q0, d, a) (exact), q = fma(r, fp32(1/d), q0).  An exhaustive check
+// over every finite fp32 a >= 2^-119 shows q equals the IEEE quotient for both
+// constants; below that the IEEE division is used.
+template <int D>
+__device__ __forceinline__ float div_by(float a) {
+  constexpr float d = (float)D;
+  constexpr float inv = 1.0f / (float)D;
+  if (a >= 0x1p-119f) {
+    const float q0 = a * inv;
+    const float r = __builtin_fmaf(-q0, d, a);
+    return __builtin_fmaf(r, inv, q0);
+  }
+  return a / d;
+}
+
 // ---------------------------------------------------------------- E4M3
 // E4M3 "FN" (bias 7, max 448, subnormals down to 2^-9).  For a value v >= 0
 // with binade E = max(floor(log2 v), -6), the representable neighbours are
@@ -72,22 +89,8 @@ __device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
 // ---------------------------------------------------------------- E2M1
 // E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}: for a in [0, 6] with binade
 // E = max(floor(log2 a), 0), neighbours are integers q in [0, 4] times
-// 2^(E-1) and the magnitude code is 2E + q.
-
-struct E2m1 {
-  uint32_t code;
-  float value;
-};
-
-// Round to nearest, ties to the even code; a must already be clipped to 6.
-__device__ __forceinline__ E2m1 e2m1_rne(float a) {
-  int E = ilog2_floor_clamped(a, 0);
-  float q = rintf(a * pow2i(1 - E));
-  E2m1 r;
-  r.code = (uint32_t)(2 * E + (int)q);
-  r.value = q * pow2i(E - 1);
-  return r;
-}
+// 2^(E-1) and the magnitude code is 2E + q.  Stochastic rounding: up iff
+// u16 < frac * 65536 with frac the exact position inside the gap.
 
 __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t u16) {
   if (a >= 6.0f) return 7u;
@@ -173,10 +176,75 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
+// ---------------------------------------------------------------- E2M1 hardware
+// gfx950's v_cvt_scalef32_pk_fp4_f32 at unit scale rounds two fp32 values to
+// E2M1 to nearest (ties to the even code), saturates at 6 and keeps the sign
+// (also of zero): exactly the nibble sign<<3 | E2M1_RNE(min(|y|, 6)).  It
+// writes byte `sel` of the packed result.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_rne(uint32_t old, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, 1.0f, SEL);
+}
+
+// 16 values -> two words of packed E2M1 codes (element 2i in the low nibble
+// of byte i).
+__device__ __forceinline__ void e2m1x16_rne(const float y[16], uint32_t &lo, uint32_t &hi) {
+  lo = e2m1x2_rne<0>(0u, y[0], y[1]);
+  lo = e2m1x2_rne<1>(lo, y[2], y[3]);
+  lo = e2m1x2_rne<2>(lo, y[4], y[5]);
+  lo = e2m1x2_rne<3>(lo, y[6], y[7]);
+  hi = e2m1x2_rne<0>(0u, y[8], y[9]);
+  hi = e2m1x2_rne<1>(hi, y[10], y[11]);
+  hi = e2m1x2_rne<2>(hi, y[12], y[13]);
+  hi = e2m1x2_rne<3>(hi, y[14], y[15]);
+}
+
+// Signed E2M1 values of the two codes in byte SEL of w (exact).
+template <int SEL>
+__device__ __forceinline__ f32x2_t e2m1x2_value(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ void e2m1x16_value(uint32_t lo, uint32_t hi, float v[16]) {
+  f32x2_t t;
+  t = e2m1x2_value<0>(lo); v[0] = t[0]; v[1] = t[1];
+  t = e2m1x2_value<1>(lo); v[2] = t[0]; v[3] = t[1];
+  t = e2m1x2_value<2>(lo); v[4] = t[0]; v[5] = t[1];
+  t = e2m1x2_value<3>(lo); v[6] = t[0]; v[7] = t[1];
+  t = e2m1x2_value<0>(hi); v[8] = t[0]; v[9] = t[1];
+  t = e2m1x2_value<1>(hi); v[10] = t[0]; v[11] = t[1];
+  t = e2m1x2_value<2>(hi); v[12] = t[0]; v[13] = t[1];
+  t = e2m1x2_value<3>(hi); v[14] = t[0]; v[15] = t[1];
+}
+
 // ---------------------------------------------------------------- lanes
+// A 128-point rotation group is held by 8 lanes of one 16-lane DPP row; the
+// group position (0..7) of a lane is given by lane bits 0, 1 and 3 (bit 2
+// tells two interleaved groups apart).  Partners in the three cross-lane
+// butterfly stages are then lane ^ 1 and lane ^ 2 (quad permutations) and
+// lane ^ 8 (rotation of the 16-lane row by 8): one DPP move each.
+__device__ __forceinline__ uint32_t group_pos(uint32_t lane) {
+  return (lane & 3u) | ((lane >> 1) & 4u);
+}
+// Lane index within a 64-lane wave -> rank of its block among the wave's 64
+// consecutive blocks, so that 8 consecutive blocks form one group.
+__device__ __forceinline__ uint32_t lane_block_rank(uint32_t lane) {
+  return (lane & 0x33u) | ((lane & 4u) << 1) | ((lane & 8u) >> 1);
+}
+
 template <int S>
 __device__ __forceinline__ float lane_xor(float v) {
-  return __shfl_xor(v, S, kWave);
+  const int x = __float_as_int(v);
+  if constexpr (S == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  } else {
+    static_assert(S == 4, "lane_xor supports group bits 1, 2, 4");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true));  // row_ror:8
+  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -216,28 +284,29 @@ __device__ __forceinline__ void fwht16_inlane(float v[16]) {
   }
 }
 
-// One cross-lane stage: lanes l and l ^ S hold coordinate blocks that are
-// 16*S apart; the lower one keeps a + b, the upper one a - b (a = lower).
+// One cross-lane stage between group positions differing in bit S: the lower
+// lane needs a + b, the upper a - b (a = the lower lane's value, b = the
+// upper's).  Every lane computes fma(own, k, partner) with k = +1 (lower) or
+// -1 (upper): the product by +-1 is exact and the fma rounds the sum once,
+// so this is exactly a + b and a - b -- signed zeros included.
 template <int S>
-__device__ __forceinline__ void fwht_cross(float v[16], uint32_t lane_in_group) {
-  const bool upper = (lane_in_group & S) != 0;
+__device__ __forceinline__ void fwht_cross(float v[16], float k) {
+  float p[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float p = lane_xor<S>(v[i]);
-    const float own = upper ? -v[i] : v[i];
-    v[i] = p + own;
-  }
+  for (int i = 0; i < 16; ++i) p[i] = lane_xor<S>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(v[i], k, p[i]);
 }
 
-// The rotation of a 128-group held by 8 consecutive lanes (16 consecutive
-// coordinates each, lane_in_group = position): stages of stride 1, ..., 64
-// in that order, then the 1/sqrt(128) normalization.  The sign flips are
+// The rotation of a 128-group held by 8 lanes (16 consecutive coordinates
+// each, `pos` = group position): stages of stride 1, ..., 64 in that order,
+// then the 1/sqrt(128) normalization.  Sign flips of the randomization are
 // applied by the caller before this.
-__device__ __forceinline__ void fwht128_group(float v[16], uint32_t lane_in_group) {
+__device__ __forceinline__ void fwht128_group(float v[16], uint32_t pos) {
   fwht16_inlane(v);
-  fwht_cross<1>(v, lane_in_group);
-  fwht_cross<2>(v, lane_in_group);
-  fwht_cross<4>(v, lane_in_group);
+  fwht_cross<1>(v, (pos & 1u) ? -1.0f : 1.0f);
+  fwht_cross<2>(v, (pos & 2u) ? -1.0f : 1.0f);
+  fwht_cross<4>(v, (pos & 4u) ? -1.0f : 1.0f);
   const float c = 0x1.6a09e6p-4f;  // fp32(1/sqrt(128)) = 0x3DB504F3
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = v[i] * c;

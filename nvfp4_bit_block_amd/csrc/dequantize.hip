@@ -19,10 +19,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 template <int OUT_BF16>
 __global__ __launch_bounds__(kThreads) void k_dequant(DequantParams p) {
   const float ts = *p.ts;
-  const uint32_t lig = threadIdx.x & 7u;
+  const uint32_t lig = group_pos(threadIdx.x & 63u);
+  const uint32_t rank = (threadIdx.x & ~63u) + lane_block_rank(threadIdx.x & 63u);
   const uint32_t sbits = p.inv_rht ? lane_sign_bits(p.sg, lig) : 0u;
   for (uint32_t base = blockIdx.x * kThreads; base < p.nblocks; base += gridDim.x * kThreads) {
-    const uint32_t gb = base + threadIdx.x;
+    const uint32_t gb = base + rank;
     const bool active = gb < p.nblocks;
     float z[16];
     if (active) {

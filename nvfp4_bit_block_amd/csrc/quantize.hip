@@ -11,14 +11,11 @@
 // the OUTPUT layout; a 128-point rotation group is 8 consecutive lanes.
 //   axis 0: a block is 16 contiguous input elements (two 16-byte loads for
 //           bf16), addressed by the flat block index.
-//   axis 1: a workgroup stages a 256 (reduction) x 128-byte (columns) tile
-//           of the row-major input in LDS, transposed, so that each lane
-//           reads its block's 16 strided elements as contiguous LDS words.
+//   axis 1: a lane loads 16 rows of one 16-byte column chunk and so holds
+//           the blocks of 8 (bf16) or 4 (fp32) columns; no LDS transpose.
 // A pass that needs the tensor-wide maximum writes one partial maximum per
 // workgroup into the workspace; the next pass reduces those partials in every
 // workgroup (no atomics, no memset, deterministic).
-#include <type_traits>
-
 #include "kernels.hpp"
 
 namespace nv4 {
@@ -95,11 +92,11 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(z[i]));
 
     if constexpr (MODE == kAmax) {
-      lmax = fmaxf(lmax, a);
+      if (active) lmax = fmaxf(lmax, a);
     } else if constexpr (MODE == kRtn || MODE == kSr) {
       // scale e = E4M3((a/6)/s_t), RNE (RTN) or rounded up (SR); codes of
       // min(|z| / (e * s_t), 6) on the E2M1 grid.
-      const float v = (a / 6.0f) / s_t;
+      const float v = div_by<6>(a) / s_t;
       const uint32_t e = (MODE == kRtn) ? e4m3_rne_sat(v) : e4m3_ceil_sat(v);
       const float r = e ? 1.0f / (e4m3_value(e) * s_t) : 0.0f;
       Philox4 u0, u1;
@@ -108,19 +105,20 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
         u1 = uniforms8(p.key, (uint64_t)gb * 2u + 1u, 0u);
       }
       uint32_t lo = 0, hi = 0;
+      if constexpr (MODE == kRtn) {
+        float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float y = fminf(fabsf(z[i] * r), 6.0f);
-        uint32_t mag = 0;
-        if (e) {
-          if constexpr (MODE == kRtn)
-            mag = e2m1_rne(y).code;
-          else
-            mag = e2m1_sr(y, uniform_at(i < 8 ? u0 : u1, i & 7));
+        for (int i = 0; i < 16; ++i) y[i] = z[i] * r;  // r = 0 when e = 0: signed zeros
+        e2m1x16_rne(y, lo, hi);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float y = fminf(fabsf(z[i] * r), 6.0f);
+          const uint32_t mag = e ? e2m1_sr(y, uniform_at(i < 8 ? u0 : u1, i & 7)) : 0u;
+          const uint32_t nib = sign_nib(z[i]) | mag;
+          if (i < 8) lo |= nib << (4 * i);
+          else hi |= nib << (4 * (i - 8));
         }
-        const uint32_t nib = sign_nib(z[i]) | mag;
-        if (i < 8) lo |= nib << (4 * i);
-        else hi |= nib << (4 * (i - 8));
       }
       if (active) {
         store_codes(p, gb, lo, hi);
@@ -128,38 +126,30 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
       }
     } else if constexpr (MODE == kIf4) {
       // both branches at their own scales; keep the smaller pairwise SSE.
-      const uint32_t ef = e4m3_rne_sat((a / 6.0f) / s_t);
+      const uint32_t ef = e4m3_rne_sat(div_by<6>(a) / s_t);
       const float Sf = e4m3_value(ef) * s_t;
       const float rf = ef ? 1.0f / Sf : 0.0f;
-      const uint32_t ei = e4m3_rne_sat((a / 7.0f) / s_t);
+      const uint32_t ei = e4m3_rne_sat(div_by<7>(a) / s_t);
       const float Si = e4m3_value(ei) * s_t;
       const float ri = ei ? 1.0f / Si : 0.0f;
-      float sqf[16], sqi[16];
-      uint32_t flo = 0, fhi = 0, ilo = 0, ihi = 0;
+      float sqf[16], sqi[16], y[16], vf[16];
+      uint32_t flo, fhi, ilo = 0, ihi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = z[i] * rf;
+      e2m1x16_rne(y, flo, fhi);
+      e2m1x16_value(flo, fhi, vf);  // signed grid values
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t sn = sign_nib(z[i]);
-        uint32_t mf = 0;
-        float vf = 0.0f;
-        if (ef) {
-          const E2m1 q = e2m1_rne(fminf(fabsf(z[i] * rf), 6.0f));
-          mf = q.code;
-          vf = q.value;
-        }
-        const float df = z[i] - (sn ? -vf : vf) * Sf;
+        const float df = z[i] - vf[i] * Sf;
         sqf[i] = df * df;
         uint32_t mi = 0;
         if (ei) mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
         const float vi = (float)mi;
         const float di = z[i] - (sn ? -vi : vi) * Si;
         sqi[i] = di * di;
-        if (i < 8) {
-          flo |= (sn | mf) << (4 * i);
-          ilo |= (sn | mi) << (4 * i);
-        } else {
-          fhi |= (sn | mf) << (4 * (i - 8));
-          ihi |= (sn | mi) << (4 * (i - 8));
-        }
+        if (i < 8) ilo |= (sn | mi) << (4 * i);
+        else ihi |= (sn | mi) << (4 * (i - 8));
       }
       const bool use_int = tree16(sqi) < tree16(sqf);
       if (active) {
@@ -169,26 +159,19 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
     } else if constexpr (MODE == kEden || MODE == kEdenFused) {
       // RTN codes under the exact scale a/6; correction c = sum z^2 /
       // sum z*zhat over the group; target t = (a/6) * c.
-      const float s_b = a / 6.0f;
+      const float s_b = div_by<6>(a);
       const float r = (a > 0.0f) ? 1.0f / s_b : 0.0f;
-      float nn[16], dd[16];
-      uint32_t lo = 0, hi = 0;
+      float nn[16], dd[16], y[16], g[16];
+      uint32_t lo, hi;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = z[i] * r;  // r = 0 when a = 0: signed zeros
+      e2m1x16_rne(y, lo, hi);
+      e2m1x16_value(lo, hi, g);  // signed grid values
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        uint32_t mag = 0;
-        float val = 0.0f;
-        if (a > 0.0f) {
-          const E2m1 q = e2m1_rne(fminf(fabsf(z[i] * r), 6.0f));
-          mag = q.code;
-          val = q.value;
-        }
-        const uint32_t sn = sign_nib(z[i]);
-        const float qv = val * s_b;
-        const float zh = sn ? -qv : qv;
+        const float zh = g[i] * s_b;
         nn[i] = z[i] * z[i];
         dd[i] = z[i] * zh;
-        if (i < 8) lo |= (sn | mag) << (4 * i);
-        else hi |= (sn | mag) << (4 * (i - 8));
       }
       float N = tree16(nn), D = tree16(dd);
       if (!p.group16) {
@@ -220,6 +203,42 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
 }
 
 // ---------------------------------------------------------------- axis 0
+// Raw input words of one lane's 16-element block.
+template <int IN_BF16>
+struct RawBlock {
+  uint4 q[IN_BF16 ? 2 : 4];
+};
+
+template <int IN_BF16>
+__device__ __forceinline__ void load_row_block(const QuantParams &p, uint32_t gb, RawBlock<IN_BF16> &b) {
+  const uint32_t r = fdiv(gb, p.k16div);
+  const uint32_t kb = gb - r * p.K16;
+  const size_t off = (size_t)r * p.ld + (size_t)kb * 16;
+  if (IN_BF16) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) b.q[i] = src[i];
+  } else {
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const float *>(p.x) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.q[i] = src[i];
+  }
+}
+
+template <int IN_BF16>
+__device__ __forceinline__ void unpack_block(const RawBlock<IN_BF16> &b, const SignMasks &sm, float z[16]) {
+  uint32_t w[IN_BF16 ? 8 : 16];
+#pragma unroll
+  for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) {
+    w[4 * i] = b.q[i].x;
+    w[4 * i + 1] = b.q[i].y;
+    w[4 * i + 2] = b.q[i].z;
+    w[4 * i + 3] = b.q[i].w;
+  }
+  if (IN_BF16) unpack_bf16(w, sm, z);
+  else unpack_f32(w, sm, z);
+}
+
 template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   __shared__ float red[kThreads / kWave];
@@ -228,36 +247,27 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
-  const uint32_t lig = threadIdx.x & 7u;
+  const uint32_t lig = group_pos(threadIdx.x & 63u);
+  // this thread's block among the workgroup's 256 consecutive blocks
+  const uint32_t rank = (threadIdx.x & ~63u) + lane_block_rank(threadIdx.x & 63u);
   const SignMasks sm = make_masks<IN_BF16>(p, lig);
+  const uint32_t stride = gridDim.x * kThreads;
   float lmax = 0.0f;
-  for (uint32_t base = blockIdx.x * kThreads; base < p.nblocks; base += gridDim.x * kThreads) {
-    const uint32_t gb = base + threadIdx.x;
+  // the next block's loads are issued before the current block is processed
+  RawBlock<IN_BF16> cur = {}, nxt = {};
+  uint32_t base = blockIdx.x * kThreads;
+  if (base + rank < p.nblocks) load_row_block<IN_BF16>(p, base + rank, cur);
+  for (; base < p.nblocks; base += stride) {
+    const uint32_t gb = base + rank;
     const bool active = gb < p.nblocks;
+    if (base + stride + rank < p.nblocks) load_row_block<IN_BF16>(p, base + stride + rank, nxt);
+    // lanes past the end hold stale values; they fill whole rotation groups
+    // and store nothing, so they never reach an output
     float z[16];
-    if (active) {
-      const uint32_t r = fdiv(gb, p.k16div);
-      const uint32_t kb = gb - r * p.K16;
-      if (IN_BF16) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const uint16_t *>(p.x) + (size_t)r * p.ld + (size_t)kb * 16);
-        const uint4 a0 = src[0], a1 = src[1];
-        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        unpack_bf16(w, sm, z);
-      } else {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const float *>(p.x) + (size_t)r * p.ld + (size_t)kb * 16);
-        const uint4 a0 = src[0], a1 = src[1], a2 = src[2], a3 = src[3];
-        const uint32_t w[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                                a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-        unpack_f32(w, sm, z);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-    }
+    unpack_block<IN_BF16>(cur, sm, z);
     if (p.rht) fwht128_group(z, lig);
     quant_block<MODE>(z, gb, active, p, s_t, lmax);
+    cur = nxt;
   }
   if constexpr (MODE == kAmax || MODE == kEden) {
     const float m = block_max(lmax, red, kThreads);
@@ -266,123 +276,77 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
 }
 
 // ---------------------------------------------------------------- axis 1
-// Tile: TT = 256 positions along the reduction (input rows) x TC columns,
-// TC * sizeof(elem) = 128 bytes.  LDS holds the tile transposed: column c's
-// 256 values are contiguous (plus a 16-byte pad).
-template <int IN_BF16>
-struct ColTile {
-  static constexpr int TT = 256;
-  static constexpr int TC = IN_BF16 ? 64 : 32;
-  static constexpr int PITCH = TT + (IN_BF16 ? 8 : 4);  // elements
-  using elem = typename std::conditional<IN_BF16 != 0, uint16_t, float>::type;
-};
-
+// A wave's tile is 128 positions along the reduction (input rows) x 128 bytes
+// of columns.  Lane (q = lane / 8, lig = lane % 8) loads the 16 rows
+// T0 + 16 lig .. + 15 of the 16-byte column chunk q: it then holds the
+// 16-element blocks of that chunk's 8 (bf16) or 4 (fp32) columns, and the 8
+// lanes with the same q hold one 128-position rotation group per column.
+// Each load instruction reads 8 rows x 128 contiguous bytes; no LDS is used.
+// The rotation sign of a position is the same for every column, so it is
+// XORed into each raw row word once.
 template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
-  using CT = ColTile<IN_BF16>;
-  using elem = typename CT::elem;
-  constexpr int TT = CT::TT, TC = CT::TC, PITCH = CT::PITCH;
-  __shared__ __attribute__((aligned(16))) elem tile[TC * PITCH];
+  constexpr int CPL = IN_BF16 ? 8 : 4;  // columns per 16-byte chunk
+  constexpr int TCOL = 8 * CPL;         // columns per wave tile
   __shared__ float red[kThreads / kWave];
-
   float s_t = 1.0f;
   if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kEdenFused) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
-  const uint32_t lig = threadIdx.x & 7u;
-  const SignMasks sm = make_masks<IN_BF16>(p, lig);
+  const uint32_t lane = threadIdx.x & 63u, lig = group_pos(lane);
+  const uint32_t q = ((lane >> 2) & 1u) | ((lane >> 4) << 1);  // column chunk of this lane
+  const uint32_t sbits = p.rht ? lane_sign_bits(p.sg, lig) : 0u;
   const uint32_t nct = p.ctiles_div.d;
+  const uint32_t waves = gridDim.x * (kThreads / kWave);
   float lmax = 0.0f;
 
-  for (uint32_t t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
+  for (uint32_t t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6); t < p.ntiles; t += waves) {
     const uint32_t tt = fdiv(t, p.ctiles_div);
     const uint32_t tc = t - tt * nct;
-    const uint32_t T0 = tt * TT, C0 = tc * TC;
-    __syncthreads();  // the previous tile's LDS reads are done
-    if (IN_BF16) {
-      // row pairs (2rp, 2rp+1) x 8 chunks of 8 columns; each thread packs
-      // the two rows of a column into one LDS word (even row in the low half).
-      const uint16_t *x = static_cast<const uint16_t *>(p.x);
-      uint32_t *tw = reinterpret_cast<uint32_t *>(tile);
-      for (uint32_t c = threadIdx.x; c < (TT / 2) * 8; c += kThreads) {
-        const uint32_t rp = c >> 3, q = c & 7u;
-        const uint32_t r0 = T0 + 2 * rp, col0 = C0 + 8 * q;
-        uint16_t v0[8], v1[8];
+    const uint32_t row0 = tt * 128 + 16 * lig;     // this lane's 16 rows
+    const uint32_t col0 = tc * TCOL + CPL * q;     // this lane's CPL columns
+    const bool rows_ok = row0 < p.rows;            // rows % 16 == 0: whole slab or nothing
+    uint32_t w[16][4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v0[j] = v1[j] = 0;
-        if (col0 < p.cols) {
-          const bool full = p.vec && col0 + 8 <= p.cols;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t r = r0 + h;
-            if (r < p.rows) {
-              const uint16_t *src = x + (size_t)r * p.ld + col0;
-              uint16_t *dst = h ? v1 : v0;
-              if (full) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(src);
-                const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                  dst[2 * j] = (uint16_t)(w[j] & 0xFFFFu);
-                  dst[2 * j + 1] = (uint16_t)(w[j] >> 16);
-                }
-              } else {
-                for (uint32_t j = 0; j < 8 && col0 + j < p.cols; ++j) dst[j] = src[j];
-              }
-            }
-          }
+    for (int r = 0; r < 16; ++r) {
+      w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0u;
+      if (rows_ok && col0 < p.cols) {
+        const size_t off = (size_t)(row0 + r) * p.ld + col0;
+        if (p.vec && col0 + CPL <= p.cols) {
+          const uint4 a = IN_BF16 ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off)
+                                  : *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.x) + off);
+          w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+        } else if (IN_BF16) {
+          const uint16_t *src = static_cast<const uint16_t *>(p.x) + off;
+          for (uint32_t j = 0; j < (uint32_t)CPL && col0 + j < p.cols; ++j)
+            w[r][j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+        } else {
+          const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const float *>(p.x) + off);
+          for (uint32_t j = 0; j < (uint32_t)CPL && col0 + j < p.cols; ++j) w[r][j] = src[j];
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          tw[((8 * q + j) * PITCH + 2 * rp) / 2] = (uint32_t)v0[j] | ((uint32_t)v1[j] << 16);
       }
-    } else {
-      const float *x = static_cast<const float *>(p.x);
-      for (uint32_t c = threadIdx.x; c < TT * 8; c += kThreads) {
-        const uint32_t r = c >> 3, q = c & 7u;
-        const uint32_t row = T0 + r, col0 = C0 + 4 * q;
-        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (row < p.rows && col0 < p.cols) {
-          const float *src = x + (size_t)row * p.ld + col0;
-          if (p.vec && col0 + 4 <= p.cols) {
-            const float4 a = *reinterpret_cast<const float4 *>(src);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-          } else {
-            for (uint32_t j = 0; j < 4 && col0 + j < p.cols; ++j) v[j] = src[j];
-          }
-        }
+      const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tile[(4 * q + j) * PITCH + r] = v[j];
-      }
+      for (int c = 0; c < 4; ++c) w[r][c] ^= sflip;
     }
-    __syncthreads();
-
-    // TC columns x 16 blocks each; a group of 8 lanes = 128 positions of one
-    // column; consecutive groups are the two halves of a column.
-    for (int round = 0; round < TC * (TT / 16) / kThreads; ++round) {
-      const uint32_t u = round * kThreads + threadIdx.x;
-      const uint32_t g = u >> 3;
-      const uint32_t c = g >> 1, h = g & 1u;
-      const uint32_t tb = h * 8 + lig;
-      const uint32_t col = C0 + c, kblk = T0 / 16 + tb;
-      const bool active = col < p.cols && kblk < p.K16;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
       float z[16];
-      if (IN_BF16) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(tile + c * PITCH + tb * 16);
-        const uint4 a0 = src[0], a1 = src[1];
-        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        unpack_bf16(w, sm, z);
-      } else {
-        const uint4 *src = reinterpret_cast<const uint4 *>(tile + c * PITCH + tb * 16);
-        const uint4 a0 = src[0], a1 = src[1], a2 = src[2], a3 = src[3];
-        const uint32_t w[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                                a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-        unpack_f32(w, sm, z);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (IN_BF16) {
+          const uint32_t v = w[r][j >> 1];
+          z[r] = (j & 1) ? bf16_hi(v) : bf16_lo(v);
+        } else {
+          z[r] = __uint_as_float(w[r][j]);
+        }
       }
       if (p.rht) fwht128_group(z, lig);
-      const uint32_t gb = col * p.K16 + kblk;
-      quant_block<MODE>(z, active ? gb : 0u, active, p, s_t, lmax);
+      const uint32_t col = col0 + j;
+      const uint32_t kblk = tt * 8 + lig;
+      const bool active = rows_ok && col < p.cols;
+      quant_block<MODE>(z, active ? col * p.K16 + kblk : 0u, active, p, s_t, lmax);
     }
   }
   if constexpr (MODE == kAmax || MODE == kEden) {
@@ -432,7 +396,9 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
 // ---------------------------------------------------------------- launch
 uint32_t quant_grid(const QuantParams &p, int in_bf16, int axis) {
   (void)in_bf16;
-  uint64_t units = axis == 0 ? ((uint64_t)p.nblocks + kThreads - 1) / kThreads : p.ntiles;
+  const uint64_t waves = kThreads / kWave;
+  uint64_t units = axis == 0 ? ((uint64_t)p.nblocks + kThreads - 1) / kThreads
+                             : ((uint64_t)p.ntiles + waves - 1) / waves;
   if (units < 1) units = 1;
   return (uint32_t)(units < (uint64_t)kMaxPartials ? units : kMaxPartials);
 }

@@ -103,7 +103,29 @@ def test_rht_values(nv, axis):
     rel = np.abs(z - ref) / np.maximum(np.abs(ref), 1e-30)
     assert np.max(np.abs(z - ref) / (np.abs(ref).max())) <= 1e-5
     assert np.mean(rel > 1e-5) <= 1e-5
+    # the kernels run the butterfly stages in the oracle's order: bit-exact,
+    # signed zeros included (exact cancellations occur on bf16 inputs)
+    assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
     torch.cuda.synchronize()
+
+
+def test_rht_signed_zero_cancellations(nv):
+    """Inputs whose rotated values cancel to exactly zero in many butterflies:
+    the sign of every zero matches the oracle."""
+    rng = np.random.default_rng(21)
+    signs = synth.signs_from_rng(rng)
+    x = np.repeat(rng.choice(np.array([1.0, -1.0, 0.5, 0.0], dtype=np.float32), (64, 8)), 16, axis=1)
+    x[:, ::3] *= -1
+    for axis in (0, 1):
+        xin = x if axis == 0 else np.ascontiguousarray(x.T)
+        z = nv.rht(to_device(xin, "bf16"), signs, axis=axis).cpu().numpy()
+        ref = oracle.rht(x, oracle.signs_words(signs))
+        assert np.count_nonzero(ref == 0) > 100
+        assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
+        for rnd, name in ((oracle.RTN, "rtn"), (oracle.MSEDEN, "mseden")):
+            g = q_to_host(nv.quantize_nvfp4(to_device(xin, "bf16"), rounding=name, axis=axis, rht_signs=signs))
+            r = oracle.quantize(xin, rounding=rnd, axis=axis, rht_on=True, signs_w=oracle.signs_words(signs))
+            assert_bit_exact(g, r, f"zero cancellations {name} axis{axis}")
 
 
 def test_tensor_scale_in(nv):
