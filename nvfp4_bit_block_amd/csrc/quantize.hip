@@ -317,13 +317,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
           const uint4 a = IN_BF16 ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off)
                                   : *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.x) + off);
           w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
-        } else if (IN_BF16) {
+        } else if (IN_BF16) {  // (fully unrolled: a runtime index would put w in scratch)
           const uint16_t *src = static_cast<const uint16_t *>(p.x) + off;
-          for (uint32_t j = 0; j < (uint32_t)CPL && col0 + j < p.cols; ++j)
-            w[r][j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+#pragma unroll
+          for (int j = 0; j < CPL; ++j)
+            if (col0 + j < p.cols) w[r][j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
         } else {
           const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const float *>(p.x) + off);
-          for (uint32_t j = 0; j < (uint32_t)CPL && col0 + j < p.cols; ++j) w[r][j] = src[j];
+#pragma unroll
+          for (int j = 0; j < CPL; ++j)
+            if (col0 + j < p.cols) w[r][j] = src[j];
         }
       }
       const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
