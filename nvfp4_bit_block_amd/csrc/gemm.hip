@@ -7,23 +7,31 @@
 // gfx950's native FP4 matrix instructions take one power-of-two (E8M0) scale
 // per 32 elements; NVFP4 has an E4M3 scale per 16.  The product of an E2M1
 // value and an E4M3 scale has at most 6 significant bits and lies in
-// [2^-10, 2688], so it is exact in fp16: each fragment is dequantized exactly
-// in registers -- v_cvt_scalef32_pk_f16_fp4 (two codes per instruction, unit
-// scale) then one packed fp16 multiply by the block scale -- and multiplied
-// on the fp16 matrix cores (v_mfma_f32_32x32x16_f16), accumulating in fp32.
+// [2^-10, 2688], so it is exact in fp16: each operand fragment is
+// dequantized exactly -- v_cvt_scalef32_pk_f16_fp4 (two codes per
+// instruction, unit scale) then one packed fp16 multiply by the block scale
+// -- and multiplied on the fp16 matrix cores (v_mfma_f32_32x32x16_f16) with
+// fp32 accumulation.
 //
-// Tiling: a workgroup of 4 waves (one per SIMD) computes a 256 x 256 tile,
-// each wave a 128 x 128 sub-tile as 4 x 4 MFMA tiles of 32 x 32 (256 fp32
-// accumulators per lane).  Operands go straight from global memory into
-// registers with buffer loads (rows past M or N read as zero): FP4 is 4x
-// smaller than the fp16 it expands to, so the two waves sharing a row panel
-// re-read it from L1/L2 instead of staging it through LDS.  K advances in
-// chunks of 128, double-buffered in registers.
+// Tiling: a workgroup of 4 waves (one per SIMD) computes a 256 x 256 tile;
+// wave (wm, wn) a 128 x 128 sub-tile as 4 x 4 MFMA tiles of 32 x 32 (256 fp32
+// accumulators per lane).  K advances in chunks of 64 (four 16-wide MFMA
+// steps).  The tile's 16 row fragments per chunk (8 of A, 8 of B, 32 rows
+// each) are split between the waves: each wave loads 4 of them (buffer
+// loads; rows past M or N read as zero), dequantizes them once, and writes
+// the fp16 MFMA operands to LDS in operand order (lane l's 16 bytes at slot
+// l: conflict-free).  Every wave then reads its 4 + 4 operands per step from
+// LDS.  So each fragment is loaded and dequantized once per workgroup, not
+// once per wave that uses it -- the dequantization is the vector-ALU cost
+// that competes with the matrix cores.  LDS is double-buffered (2 x 64 KB):
+// chunk c+1 is dequantized, one step at a time, between the MFMA steps of
+// chunk c, and the raw codes of chunk c+3 are loaded as soon as a register
+// buffer frees up; one barrier per chunk.
 //
 // K order inside a chunk: MFMA lane half h = lane / 32 holds k slots
-// 8h .. 8h+7 of each 16-wide step.  A lane loads the 64 codes at
-// k0 + 64h .. k0 + 64h + 63 (32 bytes) and feeds dword j of them to step j.
-// A and B use the same assignment, so the permutation of k cancels.
+// 8h .. 8h+7 of each 16-wide step.  A lane loads the 32 codes at
+// k0 + 32h .. k0 + 32h + 31 and feeds dword j of them to step j.  A and B use
+// the same assignment, so the permutation of k cancels.
 //
 // Workgroup order: workgroups are dispatched round-robin to the 8 XCDs; the
 // logical tile index is remapped so that each XCD receives a contiguous run,
@@ -38,71 +46,59 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kTile = 256, kWaveTile = 128, kChunk = 128, kGroupM = 4, kXcds = 8;
+constexpr uint32_t kTile = 256, kWaveTile = 128, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;
 
-struct Chunk {
-  u32x4_t code[8][2];  // fragments 0..3 = A, 4..7 = B: 64 codes each
-  uint32_t scale[8];   // the four E4M3 bytes of those 64 codes
+// Raw codes of this wave's 4 fragments for one chunk: the lane's 32 codes and
+// the chunk's four E4M3 scale bytes of its row -- bytes 2h, 2h+1 are the lane
+// half's (own fragments 0,1 = A, 2,3 = B).
+struct Raw {
+  u32x4_t code[4];
+  uint32_t scale[4];
 };
 
 struct Panels {
   __amdgpu_buffer_rsrc_t ac, as, bc, bs;  // codes / scales of this tile's rows
-  uint32_t a_soff_c[4], a_soff_s[4], b_soff_c[4], b_soff_s[4];  // fragment row offsets
-  uint32_t voff_c, voff_s;  // lane row offset within a fragment, + the lane half's k
-  uint32_t row_c, row_s;    // lane row offset without the k part (generic loads)
-  uint32_t K;
-  uint32_t h;
+  // Byte offset of this lane's row of own fragment 0 / 1 (the same rows of A
+  // and of B) and of its lane half's first k.  The whole row offset is in the
+  // vector offset, so rows past M or N fall outside the buffer's range and
+  // read as zero; the chunk's k offset (< one row) is the scalar offset.
+  uint32_t vo_c[2], vo_s[2];
+  uint32_t K, h;
 };
 
-__device__ __forceinline__ u32x4_t ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint32_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_c(const Panels &p, int o) { return o < 2 ? p.ac : p.bc; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_s(const Panels &p, int o) { return o < 2 ? p.as : p.bs; }
 
-// Whole chunk, rows 16-byte (codes) and 4-byte (scales) aligned: K % 64 == 0.
-__device__ __forceinline__ void load_fast(Chunk &c, const Panels &p, uint32_t k0) {
-  const uint32_t vc = p.voff_c + k0 / 2, vs = p.voff_s + k0 / 16;
+// Whole chunk at k0 < K, K % 64 == 0.
+__device__ __forceinline__ void load_fast(Raw &r, const Panels &p, uint32_t k0) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    c.code[f][0] = ld128(p.ac, vc, p.a_soff_c[f]);
-    c.code[f][1] = ld128(p.ac, vc + 16, p.a_soff_c[f]);
-    c.scale[f] = ld32(p.as, vs, p.a_soff_s[f]);
-    c.code[4 + f][0] = ld128(p.bc, vc, p.b_soff_c[f]);
-    c.code[4 + f][1] = ld128(p.bc, vc + 16, p.b_soff_c[f]);
-    c.scale[4 + f] = ld32(p.bs, vs, p.b_soff_s[f]);
+  for (int o = 0; o < 4; ++o) {
+    r.code[o] = __builtin_amdgcn_raw_buffer_load_b128(own_rsrc_c(p, o), p.vo_c[o & 1], k0 / 2, 0);
+    r.scale[o] = __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_s(p, o), p.vo_s[o & 1], k0 / 16, 0);
   }
 }
 
-// Any chunk, any K % 16 == 0: dword- and byte-granular loads, zero past K.
-__device__ __forceinline__ void load_generic(Chunk &c, const Panels &p, uint32_t k0) {
-  const uint32_t kl = k0 + 64 * p.h;  // first k of this lane's 64
+// Any chunk at k0 < K, K % 16 == 0: dword- and byte-granular loads, zero past K.
+__device__ __forceinline__ void load_generic(Raw &r, const Panels &p, uint32_t k0) {
+  const uint32_t kl = k0 + 32 * p.h;  // first k of this lane's 32
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const __amdgpu_buffer_rsrc_t rc = f < 4 ? p.ac : p.bc;
-    const __amdgpu_buffer_rsrc_t rs = f < 4 ? p.as : p.bs;
-    const uint32_t sc = f < 4 ? p.a_soff_c[f] : p.b_soff_c[f - 4];
-    const uint32_t ss = f < 4 ? p.a_soff_s[f] : p.b_soff_s[f - 4];
-    uint32_t w[8];
+  for (int o = 0; o < 4; ++o) {
+    uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t k = kl + 8 * q;
-      w[q] = (k + 8 <= p.K) ? ld32(rc, p.row_c + k / 2, sc) : 0u;
-    }
-    c.code[f][0] = u32x4_t{w[0], w[1], w[2], w[3]};
-    c.code[f][1] = u32x4_t{w[4], w[5], w[6], w[7]};
+    for (int q = 0; q < 4; ++q)
+      w[q] = (kl + 8 * q + 8 <= p.K)
+                 ? __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_c(p, o), p.vo_c[o & 1] + 4 * q, k0 / 2, 0)
+                 : 0u;
+    r.code[o] = u32x4_t{w[0], w[1], w[2], w[3]};
     uint32_t s = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t k = kl + 16 * q;
-      if (k < p.K) s |= ld8(rs, p.row_s + k / 16, ss) << (8 * q);
-    }
-    c.scale[f] = s;
+    for (int q = 0; q < 2; ++q)
+      if (kl + 16 * q < p.K)
+        s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(own_rsrc_s(p, o), p.vo_s[o & 1] + 2 * p.h + q,
+                                                            k0 / 16, 0)
+             << (8 * (q + 2 * p.h));
+    r.scale[o] = s;
   }
 }
 
@@ -116,41 +112,102 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 s) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ uint32_t word(const Chunk &c, int f, int j) {
-  const u32x4_t &v = c.code[f][j >> 2];
-  return v[j & 3];
+// LDS stage: [buffer][fragment 0..15 (A 0..7, B 8..15)][step][lane] x 16 bytes.
+typedef half8_t Stage[2][16][kSteps][64];
+
+// The two fp16 block scales of this lane half (bytes 2h, 2h+1 of the word).
+__device__ __forceinline__ void scales16(const Raw &r, uint32_t h, half2_t (&s)[4]) {
+#pragma unroll
+  for (int o = 0; o < 4; ++o) s[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.scale[o] >> (16 * h), 1.0f, false);
 }
 
-__device__ __forceinline__ void compute_chunk(const Chunk &c, float16_t (&acc)[4][4]) {
-  // four fp16 scales per fragment (E4M3 -> fp16 is exact)
-  half2_t s[8][2];
+// Dequantize item q = 4 * step + own fragment (0..15) of a chunk into buffer b.
+__device__ __forceinline__ void dequant_item(Stage &st, int b, const Raw &r, const half2_t (&s)[4], uint32_t w,
+                                             uint32_t lane, int q) {
+  const int j = q >> 2, o = q & 3;
+  const int frag = o < 2 ? (int)(2 * w) + o : 8 + (int)(2 * w) + (o - 2);
+  st[b][frag][j][lane] = dequant8(r.code[o][j], s[o][j >> 1]);
+}
+
+struct Ops {
+  half8_t a[4], b[4];
+};
+
+__device__ __forceinline__ void read_ops(Ops &op, const Stage &st, int b, uint32_t wm, uint32_t wn, uint32_t lane,
+                                         int j) {
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    s[f][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.scale[f], 1.0f, false);
-    s[f][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.scale[f], 1.0f, true);
+  for (int n = 0; n < 4; ++n) op.b[n] = st[b][8 + 4 * wn + n][j][lane];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) op.a[m] = st[b][4 * wm + m][j][lane];
+}
+
+__device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op.a[m], op.b[n], acc[m][n], 0, 0, 0);
+}
+
+// Interleave one step: each MFMA followed by up to NV vector-ALU instructions
+// and one LDS access.
+template <int NV>
+__device__ __forceinline__ void interleave_step() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);   // LDS
   }
+}
+
+// One chunk of the steady state.  On entry `op` holds step 0 of chunk c (in
+// buffer c&1) and `rd` the raw codes of chunk c+1.  Steps 0-2 dequantize
+// chunk c+1 into the other buffer while computing; the barrier after step 2
+// publishes it (and retires every read of this chunk's buffer), so step 3
+// can already fetch chunk c+1's first operands.  `rd` is then reloaded with
+// chunk `k_next` (clamped into range by the caller).
+__device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Raw &rd, Ops &op, const Panels &p,
+                                      uint32_t w, uint32_t wm, uint32_t wn, uint32_t lane,
+                                      float16_t (&acc)[4][4]) {
+  const int cur = c & 1, nxt = cur ^ 1;
+  half2_t s[4];
+  scales16(rd, p.h, s);
+  Ops nx;
+  // step 0
+  read_ops(nx, st, cur, wm, wn, lane, 1);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int q = j >> 1;  // 16-block of this step
-    half8_t b[4];
+  for (int q = 0; q < 6; ++q) dequant_item(st, nxt, rd, s, w, lane, q);
+  mfma16(op, acc);
+  interleave_step<3>();
+  __builtin_amdgcn_sched_barrier(0);
+  // step 1
+  read_ops(op, st, cur, wm, wn, lane, 2);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) b[n] = dequant8(word(c, 4 + n, j), s[4 + n][q >> 1][q & 1]);
+  for (int q = 6; q < 11; ++q) dequant_item(st, nxt, rd, s, w, lane, q);
+  mfma16(nx, acc);
+  interleave_step<3>();
+  __builtin_amdgcn_sched_barrier(0);
+  // step 2
+  read_ops(nx, st, cur, wm, wn, lane, 3);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const half8_t a = dequant8(word(c, m, j), s[m][q >> 1][q & 1]);
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[n], acc[m][n], 0, 0, 0);
-    }
-    // keep the scheduler from hoisting later steps' dequantization (register
-    // pressure) above this step's matrix instructions
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  for (int q = 11; q < 16; ++q) dequant_item(st, nxt, rd, s, w, lane, q);
+  mfma16(op, acc);
+  interleave_step<3>();
+  __builtin_amdgcn_sched_barrier(0);
+  load_fast(rd, p, k_next);
+  __syncthreads();
+  // step 3
+  read_ops(op, st, nxt, wm, wn, lane, 0);
+  mfma16(nx, acc);
+  interleave_step<0>();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int OUT_BF16, int FAST>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ Stage st;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t r32 = lane & 31u, h = lane >> 5;
 
@@ -169,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
   const uint32_t K = p.K, K2 = K / 2, K16 = K / 16;
   const uint32_t m0 = tm * kTile, n0 = tn * kTile;
   const uint32_t rows_a = min(kTile, p.M - m0), rows_b = min(kTile, p.N - n0);
-  const uint32_t wm = wave >> 1, wn = wave & 1u;
+  const uint32_t wm = w >> 1, wn = w & 1u;
 
   Panels P;
   P.ac = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_codes + (size_t)m0 * K2), (short)0,
@@ -181,17 +238,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
   P.bs = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_scales + (size_t)n0 * K16), (short)0,
                                            (int)(rows_b * K16), kRsrcWord3);
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const uint32_t ra = wm * kWaveTile + 32 * f, rb = wn * kWaveTile + 32 * f;
-    P.a_soff_c[f] = ra * K2;
-    P.a_soff_s[f] = ra * K16;
-    P.b_soff_c[f] = rb * K2;
-    P.b_soff_s[f] = rb * K16;
+  for (int o = 0; o < 2; ++o) {
+    const uint32_t row = 32 * (2 * w + o) + r32;  // this lane's row of own fragment o (A) and o+2 (B)
+    P.vo_c[o] = row * K2 + 16 * h;
+    P.vo_s[o] = row * K16;
   }
-  P.row_c = r32 * K2;
-  P.row_s = r32 * K16;
-  P.voff_c = P.row_c + 32 * h;
-  P.voff_s = P.row_s + 4 * h;
   P.K = K;
   P.h = h;
 
@@ -203,24 +254,57 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.0f;
 
-  const uint32_t nchunks = (K + kChunk - 1) / kChunk;
-  const uint32_t nfull = K / kChunk;
-  auto load = [&](Chunk &c, uint32_t ci) {
-    if (FAST && ci < nfull)
-      load_fast(c, P, ci * kChunk);
-    else
-      load_generic(c, P, ci * kChunk);
-  };
-  Chunk c0, c1;
-  load(c0, 0);
-  uint32_t ci = 0;
-  for (; ci + 1 < nchunks; ci += 2) {
-    load(c1, ci + 1);
-    compute_chunk(c0, acc);
-    if (ci + 2 < nchunks) load(c0, ci + 2);
-    compute_chunk(c1, acc);
+  const uint32_t nfull = FAST ? K / kChunk : 0;
+  if (nfull > 0) {
+    // Prologue: chunk 0 into buffer 0; chunk 1 in r1 and chunk 2 in r0
+    // (loads of chunks past the end re-read the last chunk, unused).
+    const uint32_t klast = (nfull - 1) * kChunk;
+    Raw r0, r1;
+    // (sched barriers keep the loads in this order, which the wait counts
+    // of the steady-state loop assume)
+    load_fast(r0, P, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_fast(r1, P, min(kChunk, klast));
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      half2_t s[4];
+      scales16(r0, P.h, s);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) dequant_item(st, 0, r0, s, w, lane, q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_fast(r0, P, min(2 * kChunk, klast));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    Ops op;
+    read_ops(op, st, 0, wm, wn, lane, 0);
+    // Steady state: chunk c+1's codes are in r1 (c even) or r0 (c odd).
+    // The chunk after the last dequantizes stale codes into the idle buffer.
+    uint32_t c = 0;
+    for (; c + 1 < nfull; c += 2) {
+      chunk(st, c, min((c + 3) * kChunk, klast), r1, op, P, w, wm, wn, lane, acc);
+      chunk(st, c + 1, min((c + 4) * kChunk, klast), r0, op, P, w, wm, wn, lane, acc);
+    }
+    if (c < nfull) chunk(st, c, klast, r1, op, P, w, wm, wn, lane, acc);
+    __syncthreads();  // every wave is done with both buffers before any reuse below
   }
-  if (ci < nchunks) compute_chunk(c0, acc);
+  // remaining K (K % 64 != 0): one chunk at a time through buffer 0
+  for (uint32_t k0 = nfull * kChunk; k0 < K; k0 += kChunk) {
+    Raw r;
+    load_generic(r, P, k0);
+    half2_t s[4];
+    scales16(r, P.h, s);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dequant_item(st, 0, r, s, w, lane, q);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < (int)kSteps; ++j) {
+      Ops op;
+      read_ops(op, st, 0, wm, wn, lane, j);
+      mfma16(op, acc);
+    }
+    __syncthreads();
+  }
 
   // ---- epilogue: D layout of a 32x32 tile -- lane holds column (lane % 32)
   // and rows 8*(e/4) + 4*h + (e%4), e = 0..15.
