@@ -48,6 +48,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget for the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="before the warm-up, run one plain fp32 negation of GIB GiB (reads and writes "
+                         "exactly that many bytes): the reference that scales the HBM byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no benchmark: read two rocprofv3 --pmc outputs of this script (FETCH_SIZE, "
+                         "then WRITE_SIZE, both run with the --copy-calibration given here) and write "
+                         "profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -73,8 +80,81 @@ def measured_traffic(kernel, digest, launch_flops_or_bytes):
     return e.get("hbm_bytes_per_launch")
 
 
+COPY_KERNEL_TAG = "neg"   # the calibration kernel's name contains this
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, counter):
+    """kernel name -> list of per-dispatch values of `counter` (summed over
+    the rows rocprofv3 writes per dispatch)."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (k, _), v in sorted(acc.items(), key=lambda kv: int(kv[0][1])):
+        out.setdefault(k, []).append(v)
+    return out
+
+
+def write_traffic(fetch_dir, write_dir, cal_gib):
+    """HBM bytes per launch of each library kernel, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled so that the calibration copy
+    reads / writes exactly its known size."""
+    fetch = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE")
+    cal = [k for k in fetch if COPY_KERNEL_TAG in k]
+    if not cal:
+        raise SystemExit("calibration kernel not found: run with --copy-calibration")
+    if cal_gib <= 0:
+        raise SystemExit("give the --copy-calibration size the counter runs used")
+    cal_bytes = float(int(cal_gib * (1 << 30)) // 4 * 4)
+    f_scale = cal_bytes / (fetch[cal[0]][0] * 1024.0)
+    w_scale = cal_bytes / (write[cal[0]][0] * 1024.0)
+    digests = {"k_gemm": source_digest("gemm.hip", "common.hpp", "kernels.hpp"),
+               "k_quant": source_digest("quantize.hip", "common.hpp", "kernels.hpp"),
+               "k_eden_scales": source_digest("quantize.hip", "common.hpp", "kernels.hpp")}
+    out = {"calibration": {"bytes": cal_bytes, "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+                           "kernel": cal[0]}}
+    for name in fetch:
+        if "nv4::" not in name:
+            continue
+        short = name.split("nv4::")[1].split("(")[0]
+        fam = next((d for d in digests if short.startswith(d)), None)
+        fb = [v * 1024.0 * f_scale for v in fetch[name]]
+        wb = [v * 1024.0 * w_scale for v in write.get(name, [0.0])]
+        fam_key = "k_gemm" if short.startswith("k_gemm") else short
+        e = out.setdefault(fam_key, {"source_digest": digests.get(fam), "instances": {}})
+        e["instances"][short] = {"launches": len(fb), "fetch_bytes": [round(x) for x in fb],
+                                 "write_bytes": [round(x) for x in wb]}
+    for k, e in out.items():
+        if k == "calibration":
+            continue
+        allf = [x for i in e["instances"].values() for x in i["fetch_bytes"]]
+        allw = [x for i in e["instances"].values() for x in i["write_bytes"]]
+        e["hbm_bytes_per_launch"] = round((sum(allf) + sum(allw)) / max(1, len(allf)))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}")
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.copy_calibration)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the quantizers and the "
                           "GEMM are single-device kernels; run with --gpus 1"}), flush=True)
@@ -167,6 +247,15 @@ def main():
         marks.append(("g", "dW", a, ev() if timed else None))
         return marks
 
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30)) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
+        print(json.dumps({"calibration_bytes": n * 4}), file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()

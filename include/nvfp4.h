@@ -176,8 +176,10 @@ int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *t
  * rows_out = N, both with the same K).  Accumulation in fp32 on the matrix
  * cores; the dequantized operands are exact in fp16, so the only rounding is
  * the accumulation's.  c: device, [M x ldc] row-major, out_dtype fp32 or bf16,
- * ldc >= N.  a_ts, b_ts: device fp32 tensor scales.  K % 16 == 0; codes and
- * scales 16-byte aligned.  IF4 operands are rejected (NVFP4_UNSUPPORTED).
+ * ldc >= N.  a_ts, b_ts: device fp32 tensor scales.  K % 16 == 0 and
+ * K <= 16777200 (else NVFP4_UNSUPPORTED); codes and scales 16-byte aligned.
+ * Operands must be NVFP4: the GEMM reads every scale byte as an E4M3 value,
+ * so IF4 output (bit 7 = INT flag) gives wrong results.
  */
 int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
                      const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,

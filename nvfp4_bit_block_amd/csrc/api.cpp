@@ -278,6 +278,10 @@ int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const floa
   if ((uint64_t)M > kMaxDim || (uint64_t)N > kMaxDim || (uint64_t)K > kMaxDim)
     return fail(NVFP4_UNSUPPORTED, "dimension above 2^31 - 1");
   if (K % 16) return fail(NVFP4_BAD_SHAPE, "K %lld is not a multiple of 16", (long long)K);
+  // a 256-row operand panel (256 * K/2 code bytes) is addressed through one
+  // buffer resource with a 32-bit byte range
+  if ((uint64_t)K * 128u > 0x7FFFFFFFull)
+    return fail(NVFP4_UNSUPPORTED, "K %lld above 16777200", (long long)K);
   if (ldc < N) return fail(NVFP4_BAD_SHAPE, "ldc %lld < N %lld", (long long)ldc, (long long)N);
   if (M == 0 || N == 0) return ok();
   if (!a_codes || !a_scales || !a_ts || !b_codes || !b_scales || !b_ts || !c)

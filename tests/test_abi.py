@@ -121,5 +121,8 @@ def test_dequantize_and_gemm_rejections(nv):
     assert g(P(FAKE), P(FAKE), P(FAKE), P(0), P(FAKE), P(FAKE), 8, 8, 64, P(FAKE), 0, 8, None) == INVALID
     assert g(P(FAKE + 4), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 64, P(FAKE), 0, 8, None) == MISALIGNED
     assert g(P(0), P(0), P(0), P(0), P(0), P(0), 0, 8, 64, P(0), 0, 8, None) == OK      # empty
+    # the 256-row operand panel must fit a 32-bit buffer range
+    assert g(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 16777216, P(FAKE), 0, 8,
+             None) == UNSUPPORTED
     assert L.nvfp4_rht(P(FAKE), 1, 4, 100, 100, 0, w, P(FAKE), None) == SHAPE
     assert L.nvfp4_rht(P(FAKE), 1, 4, 128, 128, 0, None, P(FAKE), None) == INVALID
