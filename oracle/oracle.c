@@ -295,14 +295,19 @@ static void nvfp4_block(const float *z, float s_t, int rounding, uint64_t seed,
   }
 }
 
-/* One branch of IF4 for a 16-block: returns the scale byte, writes nibbles
- * into nib[], and the pairwise sum of squared errors into *sse.
- * fp branch: E2M1 values, scale a/6; int branch: integers 0..7, scale a/7
- * (the NVINT4 row of [IF4 Table 1], maximum 7 x 448). */
-static int if4_branch(const float *z, float s_t, int is_int, int nib[16], float *sse) {
+/* One candidate coding of a 16-block: returns the scale byte, writes nibbles
+ * into nib[], and the pairwise sum of squared errors into *sse.  The block
+ * maximum is mapped to `top`:
+ *   fp branch of IF4 and NVFP4: E2M1 values, top 6;
+ *   int branch of IF4: integers 0..7, top 7 (the NVINT4 row of [IF4 Table 1],
+ *   maximum 7 x 448);
+ *   second candidate of Four Over Six: E2M1 values, top 4.
+ * Magnitudes are clamped to the largest code (6 or 7). */
+static int block_candidate(const float *z, float s_t, int is_int, float top, int nib[16],
+                           float *sse) {
   float a = 0.0f;
   for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(z[i]));
-  float top = is_int ? 7.0f : 6.0f;
+  float vmax = is_int ? 7.0f : 6.0f;
   int e = orc_e4m3_rne_sat((a / top) / s_t);
   float S = orc_e4m3_value(e) * s_t;
   float r = (e != 0) ? 1.0f / S : 0.0f;
@@ -310,7 +315,7 @@ static int if4_branch(const float *z, float s_t, int is_int, int nib[16], float 
   for (int i = 0; i < 16; i++) {
     int mag = 0;
     if (e != 0) {
-      float y = fminf(fabsf(z[i] * r), top);
+      float y = fminf(fabsf(z[i] * r), vmax);
       mag = is_int ? orc_int4_rne(y) : orc_e2m1_rne(y);
     }
     float val = is_int ? (float)mag : GRID_E2M1[mag];
@@ -335,16 +340,40 @@ static void if4_block(const float *z, float s_t, int format, uint8_t *codes_row,
                       int64_t k0, uint8_t *scale_out) {
   int nf[16], ni[16];
   float sse_f = 0.0f, sse_i = 0.0f;
-  int ei = if4_branch(z, s_t, 1, ni, &sse_i);
+  int ei = block_candidate(z, s_t, 1, 7.0f, ni, &sse_i);
   if (format == ORC_FMT_NVINT4) {
     *scale_out = (uint8_t)ei;
     for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, ni[i]);
     return;
   }
-  int ef = if4_branch(z, s_t, 0, nf, &sse_f);
+  int ef = block_candidate(z, s_t, 0, 6.0f, nf, &sse_f);
   int use_int = sse_i < sse_f;
   *scale_out = (uint8_t)(use_int ? (ei | 0x80) : ef);
   for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, use_int ? ni[i] : nf[i]);
+}
+
+/* Four Over Six, the local scaling option of the forward pass
+ * [QII-sum "Quantisierung im Vorwaertsdurchlauf"; IF4 Table 1, row
+ * "NVFP4 (4/6)": maximum 6 x 256, relative dynamic range 57.1 %].
+ * READING: each 16-block is coded twice with RTN, its maximum mapped to 6
+ * (the NVFP4 scale a/6) and to 4 (scale a/4, which moves the near-maximal
+ * values off the coarse top of the grid); the block keeps the candidate with
+ * the smaller pairwise squared error (tie: 6).  Codes and scale bytes are
+ * plain NVFP4, so dequantization is unchanged.  The tensor scale maps the
+ * absmax to 6 x 256, so that the candidate-4 scale (up to 384) still fits
+ * E4M3.
+ * Pinned by: Table 1 MSE of NVFP4 (4/6) on N(0,1) [IF4 Table 1]; per block
+ * never worse than NVFP4 RTN at the same tensor scale; the choice is the
+ * smaller of the two candidates' float64 squared errors. */
+static void fos_block(const float *z, float s_t, uint8_t *codes_row, int64_t k0,
+                      uint8_t *scale_out) {
+  int n6[16], n4[16];
+  float sse6 = 0.0f, sse4 = 0.0f;
+  int e6 = block_candidate(z, s_t, 0, 6.0f, n6, &sse6);
+  int e4 = block_candidate(z, s_t, 0, 4.0f, n4, &sse4);
+  int use4 = sse4 < sse6;
+  *scale_out = (uint8_t)(use4 ? e4 : e6);
+  for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, use4 ? n4[i] : n6[i]);
 }
 
 /* MS-EDEN, first half, for one correction group of G elements (G = 128, the
@@ -410,7 +439,7 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
                  uint8_t *codes, uint8_t *scales, float *ts_out,
                  float *z_out, float *tb_out) {
   if (!x || !codes || !scales || !ts_out) return ORC_BAD_ARG;
-  if (format < 0 || format > 2 || rounding < 0 || rounding > 2 || axis < 0 || axis > 1)
+  if (format < 0 || format > 3 || rounding < 0 || rounding > 2 || axis < 0 || axis > 1)
     return ORC_BAD_ARG;
   if (format != ORC_FMT_NVFP4 && rounding != ORC_RTN) return ORC_BAD_ARG;
   if (rows < 0 || cols < 0 || ld < cols) return ORC_BAD_SHAPE;
@@ -443,7 +472,8 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
   if (rounding != ORC_MSEDEN) {
     /* 2. tensor scale: absmax over the (rotated) tensor, mapped to the
      * largest representable magnitude [IF4 Table 1: 6 x 448 for NVFP4 and
-     * IF4, 7 x 448 for NVINT4]; an all-zero tensor takes scale 1. */
+     * IF4, 7 x 448 for NVINT4, 6 x 256 for NVFP4 (4/6)]; an all-zero tensor
+     * takes scale 1. */
     float s_t;
     if (ts_in) {
       s_t = *ts_in;
@@ -451,7 +481,9 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
       float m = 0.0f;
 #pragma omp parallel for reduction(max : m) schedule(static)
       for (int64_t i = 0; i < R * K; i++) m = fmaxf(m, fabsf(Z[i]));
-      float top = (format == ORC_FMT_NVINT4) ? 7.0f * 448.0f : 6.0f * 448.0f;
+      float top = (format == ORC_FMT_NVINT4)         ? 7.0f * 448.0f
+                  : (format == ORC_FMT_NVFP4_4OVER6) ? 6.0f * 256.0f
+                                                     : 6.0f * 448.0f;
       s_t = (m > 0.0f) ? m / top : 1.0f;
     }
     *ts_out = s_t;
@@ -464,6 +496,8 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
         if (format == ORC_FMT_NVFP4)
           nvfp4_block(zb, s_t, rounding, seed, stream, (uint64_t)(r * K + k), codes + r * (K / 2),
                       k, sc);
+        else if (format == ORC_FMT_NVFP4_4OVER6)
+          fos_block(zb, s_t, codes + r * (K / 2), k, sc);
         else
           if4_block(zb, s_t, format, codes + r * (K / 2), k, sc);
       }

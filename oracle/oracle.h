@@ -22,7 +22,8 @@ extern "C" {
 #endif
 
 /* element formats */
-enum { ORC_FMT_NVFP4 = 0, ORC_FMT_IF4 = 1, ORC_FMT_NVINT4 = 2 };
+enum { ORC_FMT_NVFP4 = 0, ORC_FMT_IF4 = 1, ORC_FMT_NVINT4 = 2,
+       ORC_FMT_NVFP4_4OVER6 = 3 /* NVFP4 codes, block maximum mapped to 6 or 4 */ };
 /* rounding of the E2M1 codes (and, for MS-EDEN, of the block scale) */
 enum { ORC_RTN = 0, ORC_SR = 1, ORC_MSEDEN = 2 };
 

@@ -91,13 +91,14 @@ def test_pairwise_sum_order(orc):
 @pytest.mark.slow
 def test_table1_mse_on_gaussian(orc):
     """Quantization MSE of N(0,1) data, Table 1 of the IF4 page (NVFP4 9.0,
-    NVINT4 7.4, IF4 6.2, x 1e-3).  Tolerance: half a unit of the last printed
+    NVFP4 (4/6) 7.5, NVINT4 7.4, IF4 6.2, x 1e-3).  Tolerance: half a unit of the last printed
     digit (0.05) plus 0.02 for the unknown sample -- the MSE moves with where
     the sample's absmax puts the block scales on the E4M3 grid (NVINT4 spans
     7.439-7.462 over twelve 4096^2 samples)."""
     x = synth.gaussian(4096, 4096, seed=0)
     want = _table1()
-    for name, fmt in (("NVFP4", orc.FMT_NVFP4), ("NVINT4", orc.FMT_NVINT4), ("IF4", orc.FMT_IF4)):
+    for name, fmt in (("NVFP4", orc.FMT_NVFP4), ("NVINT4", orc.FMT_NVINT4), ("IF4", orc.FMT_IF4),
+                      ("NVFP4_4over6", orc.FMT_NVFP4_4OVER6)):
         q = orc.quantize(x, fmt=fmt)
         d = orc.dequantize(q["codes"], q["scales"], q["ts"], fmt=fmt)
         mse = float(np.mean((d.astype(np.float64) - x) ** 2)) * 1e3
@@ -238,6 +239,91 @@ def test_if4_selection_is_bruteforce_minimum(orc):
             if abs(sse["fp"] - sse["int"]) > 1e-3 * best:
                 assert flag == (1 if sse["int"] < sse["fp"] else 0)
     assert 0 < n_int < x.size // 16   # both branches occur on heavy-tailed rows
+
+
+def _fos_candidates(orc, z, ts):
+    """Both Four Over Six candidates of one block, in float64: the block
+    maximum mapped to 6 and to 4, elementwise nearest E2M1 code (brute force),
+    magnitudes clamped to 6.  Returns {top: (scale byte, squared error)}."""
+    e4 = np.array([orc.e4m3_value(b) for b in range(128)], dtype=np.float64)
+    grid = np.array([orc.e2m1_value(c) for c in range(8)], dtype=np.float64)
+    a = np.float32(np.abs(z).max())
+    out = {}
+    for top in (6.0, 4.0):
+        e = orc.e4m3_rne(np.float32(np.float32(a / np.float32(top)) / np.float32(ts)))
+        S = e4[e] * np.float64(np.float32(ts))
+        if e == 0:
+            rec = np.zeros(16)
+        else:
+            y = np.minimum(np.abs(z) / S, 6.0)
+            rec = np.sign(z) * grid[np.argmin(np.abs(y[:, None] - grid[None, :]), axis=1)] * S
+        out[top] = (e, ((z - rec) ** 2).sum())
+    return out
+
+
+def test_four_over_six_tensor_scale_and_range(orc):
+    """Four Over Six maps the absmax to 6 x 256 (IF4 Table 1, row NVFP4 (4/6)):
+    the absmax block's scale is 256 (6-candidate) or 384 (4-candidate), no
+    block scale exceeds 384 (inside E4M3), and codes and scales are plain
+    NVFP4."""
+    x = synth.gaussian(64, 512, seed=21)
+    m = np.float32(np.abs(x).max())
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4_4OVER6)
+    assert q["ts"] == m / np.float32(1536.0)
+    assert np.all(q["scales"] < 0x80)
+    vals = np.array([orc.e4m3_value(int(b)) for b in q["scales"].ravel()])
+    assert vals.max() <= 384.0
+    r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert orc.e4m3_value(int(q["scales"][r, c // 16])) in (256.0, 384.0)
+    # the NVFP4 dequantizer reads it: the reconstruction error is that of
+    # the chosen candidate
+    d = orc.dequantize(q["codes"], q["scales"], q["ts"], fmt=orc.FMT_NVFP4)
+    d46 = orc.dequantize(q["codes"], q["scales"], q["ts"], fmt=orc.FMT_NVFP4_4OVER6)
+    assert np.array_equal(d, d46)
+
+
+def test_four_over_six_choice_is_bruteforce_minimum(orc):
+    """Per 16-block the kept candidate has the smaller squared error of the two
+    (float64 brute force); near-ties are left to the fp32 decision.  Both
+    candidates occur on Gaussian data."""
+    x = synth.gaussian(48, 512, seed=22)
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4_4OVER6)
+    ts = float(q["ts"])
+    d = orc.dequantize(q["codes"], q["scales"], q["ts"], fmt=orc.FMT_NVFP4).astype(np.float64)
+    n4 = 0
+    for r in range(x.shape[0]):
+        for b in range(x.shape[1] // 16):
+            z = x[r, 16 * b:16 * b + 16].astype(np.float64)
+            cand = _fos_candidates(orc, z, ts)
+            got = ((z - d[r, 16 * b:16 * b + 16]) ** 2).sum()
+            best = min(v[1] for v in cand.values())
+            assert got <= best * (1 + 1e-5) + 1e-30
+            s6, s4 = cand[6.0][1], cand[4.0][1]
+            if abs(s6 - s4) > 1e-3 * best:
+                want = cand[4.0][0] if s4 < s6 else cand[6.0][0]
+                assert q["scales"][r, b] == want
+                n4 += int(s4 < s6)
+    assert 0 < n4 < x.size // 16
+
+
+def test_four_over_six_never_worse_than_rtn_at_same_scale(orc):
+    """With the tensor scale fixed, the 6-candidate is exactly NVFP4 RTN, so
+    Four Over Six never has a larger block error; where a block keeps the
+    6-candidate its codes and scale equal RTN's."""
+    x = synth.gradient(64, 512, seed=23)[0]
+    ts = float(np.float32(np.abs(x).max()) / np.float32(1536.0))
+    q46 = orc.quantize(x, fmt=orc.FMT_NVFP4_4OVER6, ts_in=ts)
+    q6 = orc.quantize(x, ts_in=ts)
+    d46 = orc.dequantize(q46["codes"], q46["scales"], q46["ts"]).astype(np.float64)
+    d6 = orc.dequantize(q6["codes"], q6["scales"], q6["ts"]).astype(np.float64)
+    e46 = ((x - d46) ** 2).reshape(-1, 16).sum(1)
+    e6 = ((x - d6) ** 2).reshape(-1, 16).sum(1)
+    assert np.all(e46 <= e6 * (1 + 1e-6) + 1e-30)
+    same = q46["scales"].ravel() == q6["scales"].ravel()
+    c46 = q46["codes"].reshape(-1, 8)
+    c6 = q6["codes"].reshape(-1, 8)
+    assert np.array_equal(c46[same], c6[same])
+    assert e46.sum() < e6.sum()
 
 
 def test_if4_int_flag_only_in_if4(orc):
