@@ -331,9 +331,37 @@ def main():
         "kernels": kernels,
     }
 
+    result["extras"] = extras(nv, torch, stream, X, W, dY, signs, outs, wss, args.steps)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xh, Wh, dYh, signs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
+    """Options beyond the step, timed on the same inputs and buffers (not part
+    of `value`): Four Over Six forward scaling of X and W."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        total = 0.0
+        for _ in range(reps):
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            total += a.elapsed_time(b)
+        return total / reps
+
+    res = {}
+    for name, x, q in (("X_4over6", X, "qX"), ("W_4over6", W, "qW")):
+        ms = timed(lambda: nv.quantize_nvfp4(x, scale_rule="4over6", out=outs[q], workspace=wss[q]))
+        gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                     "shape_in": list(x.shape), "what": "RTN, Four Over Six block scaling, axis 0"}
+    return res
 
 
 def cpu_baseline(Xh, Wh, dYh, signs, budget_s):

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -87,6 +87,13 @@ typedef enum nvfp4_rounding {
 
 typedef enum nvfp4_format { NVFP4_FORMAT_NVFP4 = 0, NVFP4_FORMAT_IF4 = 1 } nvfp4_format;
 
+/* How an RTN block scale is chosen (nvfp4_quantize_nvfp4 only). */
+typedef enum nvfp4_scale_rule {
+  NVFP4_SCALE_MAX6 = 0,    /* block maximum mapped to 6: e = E4M3((a/6)/s_t)   */
+  NVFP4_SCALE_4OVER6 = 1   /* Four Over Six: the better of maximum -> 6 and
+                              maximum -> 4, s_t = max|z| / (6 * 256)           */
+} nvfp4_scale_rule;
+
 typedef struct nvfp4_opts {
   int32_t rounding;        /* nvfp4_rounding                                   */
   int32_t axis;            /* 0 or 1, see above                                */
@@ -99,10 +106,11 @@ typedef struct nvfp4_opts {
   int32_t eden_group;      /* MS-EDEN correction group: 128 (default) or 16    */
   const float *tensor_scale_in; /* DEVICE pointer to a given fp32 tensor scale,
                               or NULL to compute it from this tensor           */
+  int32_t scale_rule;      /* nvfp4_scale_rule; NVFP4_SCALE_4OVER6 needs RTN   */
 } nvfp4_opts;
 
 /* Fills *o with defaults: RTN, axis 0, no rotation, seed 0, stream 0,
- * eden_group 128, computed tensor scale. */
+ * eden_group 128, computed tensor scale, scale rule NVFP4_SCALE_MAX6. */
 void nvfp4_opts_init(nvfp4_opts *o);
 
 /* Bytes of device workspace the quantizers need for this shape and options
@@ -128,6 +136,13 @@ size_t nvfp4_workspace_size(int64_t rows, int64_t cols, const nvfp4_opts *o);
  *      c = sum z^2 / sum z*zhat; target t = (a/6)*c; s_t = max t / 448;
  *      scale e = SR of min(t/s_t, 448) onto the E4M3 grid (Philox tag 1,
  *      one uniform per block).
+ *   4. RTN with scale_rule NVFP4_SCALE_4OVER6 (Four Over Six, the local
+ *      scaling option of the forward pass [QII-sum "Quantisierung im
+ *      Vorwaertsdurchlauf"; IF4 Table 1, row "NVFP4 (4/6)"]): s_t =
+ *      max|z| / (6 * 256); every block is coded by RTN twice, with
+ *      e = E4M3((a/6)/s_t) and with e = E4M3((a/4)/s_t), and keeps the one
+ *      with the smaller pairwise sum of squared errors (ties keep a/6).
+ *      Output is plain NVFP4 (dequantize with NVFP4_FORMAT_NVFP4).
  * x: device, in_dtype elements, row-major with leading dimension ld >= cols
  * (elements).  axis 0 needs a 16-byte aligned base and ld * sizeof(elem) a
  * multiple of 16; axis 1 needs only element alignment (16-byte aligned rows

@@ -17,11 +17,12 @@ import numpy as np
 __all__ = [
     "RTN", "SR", "MSEDEN", "FORMAT_NVFP4", "FORMAT_IF4", "QTensor", "NvFp4Error",
     "lib", "signs_to_words", "workspace_size", "quantize_nvfp4", "quantize_if4",
-    "dequantize", "gemm_nvfp4", "rht", "abi_version",
+    "dequantize", "gemm_nvfp4", "rht", "abi_version", "SCALE_MAX6", "SCALE_4OVER6",
 ]
 
 RTN, SR, MSEDEN = 0, 1, 2
 FORMAT_NVFP4, FORMAT_IF4 = 0, 1
+SCALE_MAX6, SCALE_4OVER6 = 0, 1
 _F32, _BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,6 +46,7 @@ class _Opts(ctypes.Structure):
         ("stream", ctypes.c_uint32),
         ("eden_group", ctypes.c_int32),
         ("tensor_scale_in", ctypes.c_void_p),
+        ("scale_rule", ctypes.c_int32),
     ]
 
 
@@ -122,7 +124,11 @@ def _dtype_code(t, torch):
     raise NvFp4Error(f"input dtype {t.dtype} is not float32 or bfloat16")
 
 
-def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in):
+_SCALE_RULE = {"max6": SCALE_MAX6, "4over6": SCALE_4OVER6, "four_over_six": SCALE_4OVER6,
+               SCALE_MAX6: SCALE_MAX6, SCALE_4OVER6: SCALE_4OVER6}
+
+
+def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule=SCALE_MAX6):
     o = _Opts()
     lib().nvfp4_opts_init(ctypes.byref(o))
     o.rounding = _ROUNDING[rounding.lower() if isinstance(rounding, str) else rounding]
@@ -136,6 +142,7 @@ def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_i
     o.stream = int(stream_id) & 0xFFFFFFFF
     o.eden_group = int(eden_group)
     o.tensor_scale_in = None if tensor_scale_in is None else tensor_scale_in.data_ptr()
+    o.scale_rule = _SCALE_RULE[scale_rule.lower() if isinstance(scale_rule, str) else scale_rule]
     return o
 
 
@@ -165,7 +172,7 @@ def workspace_size(rows, cols, rounding=RTN, axis=0, tensor_scale_in=None):
 
 
 def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in,
-              out, workspace, fmt):
+              out, workspace, fmt, scale_rule=SCALE_MAX6):
     import torch
     L = lib()
     if x.dim() != 2:
@@ -176,7 +183,7 @@ def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, ten
         raise NvFp4Error("x must have unit stride along its last dimension")
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
-    o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in)
+    o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule)
     R, K = (rows, cols) if axis == 0 else (cols, rows)
     dev = x.device
     if out is None:
@@ -197,12 +204,13 @@ def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, ten
 
 
 def quantize_nvfp4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0, eden_group=128,
-                   tensor_scale_in=None, out=None, workspace=None):
+                   tensor_scale_in=None, out=None, workspace=None, scale_rule=SCALE_MAX6):
     """NVFP4 quantization of a 2-D float32/bfloat16 device tensor (see
     ``nvfp4_quantize_nvfp4`` in include/nvfp4.h).  rht_signs: 128 flags or 4
-    words enable the randomized Hadamard rotation.  Returns a QTensor."""
+    words enable the randomized Hadamard rotation.  scale_rule "4over6"
+    selects Four Over Six block scaling (RTN only).  Returns a QTensor."""
     return _quantize(lib().nvfp4_quantize_nvfp4, x, rounding, axis, rht_signs, seed, stream_id,
-                     eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4)
+                     eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4, scale_rule)
 
 
 def quantize_if4(x, axis=0, rht_signs=None, tensor_scale_in=None, out=None, workspace=None):

@@ -16,7 +16,8 @@ enum Mode : int {
   kIf4 = 3,        // IF4 selection (RTN in both branches)
   kEden = 4,       // MS-EDEN pass 1: codes + target scales + partial maxima
   kEdenFused = 5,  // MS-EDEN with a given tensor scale: codes + scales in one pass
-  kRot = 6         // rotation only: rotated fp32 values
+  kRot = 6,        // rotation only: rotated fp32 values
+  kFos = 7         // NVFP4 RTN, Four Over Six block scale (maximum -> 6 or 4)
 };
 
 constexpr int kThreads = 256;      // threads per workgroup of every quantizer

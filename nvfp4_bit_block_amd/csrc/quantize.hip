@@ -156,6 +156,39 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
         store_codes(p, gb, use_int ? ilo : flo, use_int ? ihi : fhi);
         p.scales[gb] = (uint8_t)(use_int ? (ei | 0x80u) : ef);
       }
+    } else if constexpr (MODE == kFos) {
+      // Four Over Six: RTN with the block maximum mapped to 6 and to 4;
+      // keep the smaller pairwise SSE (tie: 6).
+      const uint32_t e6 = e4m3_rne_sat(div_by<6>(a) / s_t);
+      const float S6 = e4m3_value(e6) * s_t;
+      const float r6 = e6 ? 1.0f / S6 : 0.0f;
+      const uint32_t e4 = e4m3_rne_sat((a * 0.25f) / s_t);
+      const float S4 = e4m3_value(e4) * s_t;
+      const float r4 = e4 ? 1.0f / S4 : 0.0f;
+      float y[16], v[16], sq6[16], sq4[16];
+      uint32_t lo6, hi6, lo4, hi4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = z[i] * r6;  // r = 0 when e = 0: signed zeros
+      e2m1x16_rne(y, lo6, hi6);
+      e2m1x16_value(lo6, hi6, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float d = z[i] - v[i] * S6;
+        sq6[i] = d * d;
+        y[i] = z[i] * r4;
+      }
+      e2m1x16_rne(y, lo4, hi4);
+      e2m1x16_value(lo4, hi4, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float d = z[i] - v[i] * S4;
+        sq4[i] = d * d;
+      }
+      const bool use4 = tree16(sq4) < tree16(sq6);
+      if (active) {
+        store_codes(p, gb, use4 ? lo4 : lo6, use4 ? hi4 : hi6);
+        p.scales[gb] = (uint8_t)(use4 ? e4 : e6);
+      }
     } else if constexpr (MODE == kEden || MODE == kEdenFused) {
       // RTN codes under the exact scale a/6; correction c = sum z^2 /
       // sum z*zhat over the group; target t = (a/6) * c.
@@ -243,7 +276,7 @@ template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
-  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kEdenFused) {
+  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kEdenFused) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
@@ -290,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   constexpr int TCOL = 8 * CPL;         // columns per wave tile
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
-  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kEdenFused) {
+  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kEdenFused) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
@@ -431,6 +464,7 @@ static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid
     case kEden: launch_one<IN_BF16, kEden>(p, axis, grid, s); break;
     case kEdenFused: launch_one<IN_BF16, kEdenFused>(p, axis, grid, s); break;
     case kRot: launch_one<IN_BF16, kRot>(p, axis, grid, s); break;
+    case kFos: launch_one<IN_BF16, kFos>(p, axis, grid, s); break;
   }
 }
 

@@ -41,7 +41,7 @@ def test_header_functions_exported(nv):
 
 def test_version_and_strings(nv):
     L = nv.lib()
-    assert nv.abi_version() == 1
+    assert nv.abi_version() == 2
     for st, text in ((OK, b"ok"), (INVALID, b"invalid argument"), (SHAPE, b"bad shape"),
                      (MISALIGNED, b"misaligned pointer or stride"), (WS_SMALL, b"workspace too small"),
                      (HIP_ERR, b"HIP error"), (UNSUPPORTED, b"unsupported")):
@@ -99,6 +99,10 @@ def test_quantize_rejections(nv):
     assert _q(nv, ws=FAKE + 16) == MISALIGNED
     assert _q(nv, ws_bytes=100) == WS_SMALL
     assert _q(nv, fn="nvfp4_quantize_if4", rounding=1) == INVALID
+    assert _q(nv, scale_rule=2) == INVALID
+    assert _q(nv, scale_rule=1, rounding=1) == INVALID        # Four Over Six: RTN only
+    assert _q(nv, scale_rule=1, rounding=2) == INVALID
+    assert _q(nv, fn="nvfp4_quantize_if4", scale_rule=1) == INVALID
     _q(nv, cols=100)
     assert b"multiple of 16" in L.nvfp4_last_error()
 

@@ -97,6 +97,21 @@ def test_mlp_step_quantizations(nv, mlp, name):
         assert_rotated_close(g, ref, what=name)
 
 
+def test_mlp_forward_four_over_six(nv, mlp):
+    """The forward pass with Four Over Six scaling of X and W: both operands
+    bit-exact at full size, then Y = X W^T on sampled entries."""
+    import torch
+    x, wt, _, _ = mlp
+    gx = nv.quantize_nvfp4(to_device(x, "bf16"), scale_rule="4over6")
+    gw = nv.quantize_nvfp4(to_device(wt, "bf16"), scale_rule="4over6")
+    rx = oracle.quantize(x, fmt=oracle.FMT_NVFP4_4OVER6)
+    rw = oracle.quantize(wt, fmt=oracle.FMT_NVFP4_4OVER6)
+    assert_bit_exact(q_to_host(gx), rx, "X 4over6")
+    assert_bit_exact(q_to_host(gw), rw, "W 4over6")
+    c = nv.gemm_nvfp4(gx, gw, out_dtype=torch.float32).cpu().numpy()
+    sampled_gemm_check(nv, rx, rw, c, seed=4)
+
+
 @pytest.mark.parametrize("which", ["Y", "dX", "dW"])
 def test_mlp_step_gemms(nv, mlp, which):
     import torch

@@ -92,6 +92,42 @@ def test_if4_bit_exact(nv, axis, dtype):
 
 
 @pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_four_over_six_bit_exact(nv, axis, dtype):
+    """Four Over Six (RTN, block maximum mapped to 6 or 4): codes, scales and
+    the tensor scale bit-exact; both candidates are taken somewhere."""
+    shapes = ROW_SHAPES if axis == 0 else COL_SHAPES
+    n4 = 0
+    for i, (r, c) in enumerate(shapes):
+        x = synth.gradient(r, c, seed=500 + i)[0] if dtype == "bf16" else synth.gaussian(r, c, seed=500 + i)
+        g = q_to_host(nv.quantize_nvfp4(to_device(x, dtype), axis=axis, scale_rule="4over6"))
+        ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_4OVER6, axis=axis)
+        assert_bit_exact(g, ref, f"4over6 {dtype} axis{axis} {r}x{c}")
+        rtn = oracle.quantize(x, axis=axis, ts_in=float(ref["ts"]))
+        n4 += int(np.sum(ref["scales"] != rtn["scales"]))
+    assert n4 > 0
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_four_over_six_rotation_and_given_scale(nv, axis):
+    import torch
+    rng = np.random.default_rng(17)
+    signs = synth.signs_from_rng(rng)
+    x = synth.gradient(256, 384, seed=510)[0]
+    if axis == 1:
+        x = np.ascontiguousarray(x[:, :256])
+    w = oracle.signs_words(signs)
+    g = q_to_host(nv.quantize_nvfp4(to_device(x, "bf16"), axis=axis, rht_signs=signs, scale_rule="4over6"))
+    ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_4OVER6, axis=axis, rht_on=True, signs_w=w)
+    assert_rotated_close(g, ref, what=f"4over6 rotation axis{axis}")
+    ts = np.float32(0.0123)
+    g = q_to_host(nv.quantize_nvfp4(to_device(x, "bf16"), axis=axis, scale_rule="4over6",
+                                    tensor_scale_in=torch.tensor([ts], device="cuda:0")))
+    ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_4OVER6, axis=axis, ts_in=float(ts))
+    assert_bit_exact(g, ref, f"4over6 given scale axis{axis}")
+
+
+@pytest.mark.parametrize("axis", [0, 1])
 def test_rht_values(nv, axis):
     import torch
     rng = np.random.default_rng(8)
