@@ -340,7 +340,8 @@ def main():
 
 def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
     """Options beyond the step, timed on the same inputs and buffers (not part
-    of `value`): Four Over Six forward scaling of X and W."""
+    of `value`): IF4 quantization of X and W and the Y GEMM on IF4 operands;
+    Four Over Six forward scaling of X and W."""
     def timed(fn):
         fn()
         torch.cuda.synchronize()
@@ -356,6 +357,22 @@ def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
         return total / reps
 
     res = {}
+    # IF4 forward operands (the output buffers of the step are reused), then
+    # the Y GEMM on them through the INT-flag-aware entry point
+    qa = nv.quantize_if4(X, out=outs["qX"], workspace=wss["qX"])
+    qb = nv.quantize_if4(W, out=outs["qW"], workspace=wss["qW"])
+    Yb = torch.empty((X.shape[0], W.shape[0]), dtype=torch.bfloat16, device=X.device)
+    ms = timed(lambda: nv.gemm_nvfp4(qa, qb, out=Yb))
+    fl = 2.0 * X.shape[0] * W.shape[0] * X.shape[1]
+    res["gemm_Y_if4"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                         "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
+                         "what": "Y = X W^T, both operands IF4 (INT-flagged blocks decoded by table)"}
+    for name, x, q in (("X_if4", X, "qX"), ("W_if4", W, "qW")):
+        ms = timed(lambda: nv.quantize_if4(x, out=outs[q], workspace=wss[q]))
+        gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                     "shape_in": list(x.shape), "what": "IF4 (FP4/INT4 per 16-group), axis 0"}
+    del Yb
     for name, x, q in (("X_4over6", X, "qX"), ("W_4over6", W, "qW")):
         ms = timed(lambda: nv.quantize_nvfp4(x, scale_rule="4over6", out=outs[q], workspace=wss[q]))
         gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9

@@ -193,13 +193,28 @@ int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *t
  * the accumulation's.  c: device, [M x ldc] row-major, out_dtype fp32 or bf16,
  * ldc >= N.  a_ts, b_ts: device fp32 tensor scales.  K % 16 == 0 and
  * K <= 16777200 (else NVFP4_UNSUPPORTED); codes and scales 16-byte aligned.
- * Operands must be NVFP4: the GEMM reads every scale byte as an E4M3 value,
- * so IF4 output (bit 7 = INT flag) gives wrong results.
+ * Operands must be NVFP4: this entry point reads every scale byte as an E4M3
+ * value, so IF4 output (bit 7 = INT flag) gives wrong results here; use
+ * nvfp4_gemm_if4 for it.
  */
 int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
                      const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
                      int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
                      void *stream);
+
+/*
+ * The same GEMM on IF4 operands [IF4 abstract, Figure 1; the IF4 page also
+ * describes an IF4 multiply-accumulate unit, Figure 6]: a block whose scale
+ * byte has bit 7 set holds sign-magnitude integers 0..7 (value
+ * +-q * E4M3(scale & 0x7F)), any other block E2M1 codes.  NVFP4 operands are
+ * valid IF4 operands (no flags), so either operand may be either format, as
+ * produced by nvfp4_quantize_if4 or nvfp4_quantize_nvfp4.  Arguments, layout,
+ * accuracy and errors as nvfp4_gemm_nvfp4.
+ */
+int nvfp4_gemm_if4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                   const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+                   int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
+                   void *stream);
 
 /*
  * The rotation alone, for checking it: out[rows_out x K] fp32 = the rotated

@@ -75,8 +75,9 @@ def lib():
         f.argtypes = [P, INT, I64, I64, I64, ctypes.POINTER(_Opts), P, P, P, P, SZ, P]
     L.nvfp4_dequantize.restype = INT
     L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, INT, P, INT, P, P]
-    L.nvfp4_gemm_nvfp4.restype = INT
-    L.nvfp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, INT, I64, P]
+    for name in ("nvfp4_gemm_nvfp4", "nvfp4_gemm_if4"):
+        getattr(L, name).restype = INT
+        getattr(L, name).argtypes = [P, P, P, P, P, P, I64, I64, I64, P, INT, I64, P]
     L.nvfp4_rht.restype = INT
     L.nvfp4_rht.argtypes = [P, INT, I64, I64, I64, INT, P, P, P]
     L.nvfp4_status_string.restype = ctypes.c_char_p
@@ -238,19 +239,21 @@ def dequantize(q, inv_rht_signs=None, out_dtype=None, out=None):
 
 
 def gemm_nvfp4(a, b, out_dtype=None, out=None):
-    """C = (ts_a ts_b) * A_hat @ B_hat^T for two K-major NVFP4 QTensors
-    (A: [M, K], B: [N, K]); C is [M, N] float32 (or bfloat16)."""
+    """C = (ts_a ts_b) * A_hat @ B_hat^T for two K-major NVFP4 or IF4
+    QTensors (A: [M, K], B: [N, K]); C is [M, N] float32 (or bfloat16)."""
     import torch
     if a.k != b.k:
         raise NvFp4Error(f"K mismatch: {a.k} vs {b.k}")
-    if a.format != FORMAT_NVFP4 or b.format != FORMAT_NVFP4:
-        raise NvFp4Error("gemm_nvfp4 takes NVFP4 operands only")
+    if a.format not in (FORMAT_NVFP4, FORMAT_IF4) or b.format not in (FORMAT_NVFP4, FORMAT_IF4):
+        raise NvFp4Error("operands must be NVFP4 or IF4 QTensors")
+    # IF4 operands go through the entry point that decodes INT-flagged blocks
+    fn = lib().nvfp4_gemm_nvfp4 if a.format == b.format == FORMAT_NVFP4 else lib().nvfp4_gemm_if4
     out_dtype = out_dtype or torch.float32
     M, N = a.rows, b.rows
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
     ldc = out.stride(0) if M > 1 else N
-    rc = lib().nvfp4_gemm_nvfp4(ctypes.c_void_p(a.codes.data_ptr()), ctypes.c_void_p(a.scales.data_ptr()),
+    rc = fn(ctypes.c_void_p(a.codes.data_ptr()), ctypes.c_void_p(a.scales.data_ptr()),
                                 ctypes.c_void_p(a.tensor_scale.data_ptr()),
                                 ctypes.c_void_p(b.codes.data_ptr()), ctypes.c_void_p(b.scales.data_ptr()),
                                 ctypes.c_void_p(b.tensor_scale.data_ptr()), M, N, a.k,

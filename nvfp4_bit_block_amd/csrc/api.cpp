@@ -275,10 +275,10 @@ int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *t
   return ok();
 }
 
-int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
-                     const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
-                     int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
-                     void *stream) {
+namespace {
+int gemm_impl(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+              const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts, int64_t M,
+              int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc, void *stream, int if4) {
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16)
     return fail(NVFP4_INVALID_ARG, "out_dtype %d is not NVFP4_F32 or NVFP4_BF16", out_dtype);
   if (M < 0 || N < 0 || K < 0) return fail(NVFP4_INVALID_ARG, "negative shape");
@@ -310,9 +310,26 @@ int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const floa
   p.M = (uint32_t)M;
   p.N = (uint32_t)N;
   p.K = (uint32_t)K;
-  hipError_t e = launch_gemm(p, out_dtype == NVFP4_BF16, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_gemm(p, out_dtype == NVFP4_BF16, if4, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+int nvfp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                     const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+                     int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
+                     void *stream) {
+  return gemm_impl(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, out_dtype, ldc,
+                   stream, 0);
+}
+
+int nvfp4_gemm_if4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                   const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+                   int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
+                   void *stream) {
+  return gemm_impl(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, out_dtype, ldc,
+                   stream, 1);
 }
 
 int nvfp4_rht(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld, int axis,

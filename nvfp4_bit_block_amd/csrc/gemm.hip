@@ -112,21 +112,76 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 s) {
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// IF4 operands: a block whose scale byte has bit 7 set holds sign-magnitude
+// integers 0..7 instead of E2M1 codes.  Every magnitude of either kind is an
+// fp16 value with a zero low byte, so one byte permute per pair of codes
+// looks up the high bytes in a 16-byte table chosen by the block's flag:
+//   E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6} -> 00 38 3C 3E 40 42 44 46
+//   INT  {0, 1, 2, 3, 4, 5, 6, 7}    -> 00 3C 40 42 44 45 46 47
+constexpr uint32_t kLutFpLo = 0x3E3C3800u, kLutFpHi = 0x46444240u;
+constexpr uint32_t kLutIntLo = 0x42403C00u, kLutIntHi = 0x47464544u;
+
+// 8 codes of one block (element 2i in the low nibble of byte i), decoded
+// through the table {lut_hi:lut_lo}, times one fp16 scale.
+__device__ __forceinline__ half8_t dequant8_lut(uint32_t w, _Float16 s, uint32_t lut_lo, uint32_t lut_hi) {
+  const half2_t s2 = {s, s};
+  const uint32_t lo_n = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi_n = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+  half8_t out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // bytes [0, code 2k, 0, code 2k+1]
+    const uint32_t h = __builtin_amdgcn_perm(hi_n, lo_n, 0x000C000Cu | ((4u + k) << 24) | ((uint32_t)k << 8));
+    // selector [zero, magnitude, zero, magnitude] -> fp16 magnitudes
+    const uint32_t sel = (h & 0x07000700u) | 0x000C000Cu;
+    const uint32_t mag = __builtin_amdgcn_perm(lut_hi, lut_lo, sel);
+    // sign bits 11 and 27 of h move to the fp16 sign bits 15 and 31
+    const uint32_t v = ((h << 4) & 0x80008000u) | mag;
+    const half2_t p = __builtin_bit_cast(half2_t, v) * s2;
+    out[2 * k] = p[0];
+    out[2 * k + 1] = p[1];
+  }
+  return out;
+}
+
 // LDS stage: [buffer][fragment 0..15 (A 0..7, B 8..15)][step][lane] x 16 bytes.
 typedef half8_t Stage[2][16][kSteps][64];
 
-// The two fp16 block scales of this lane half (bytes 2h, 2h+1 of the word).
-__device__ __forceinline__ void scales16(const Raw &r, uint32_t h, half2_t (&s)[4]) {
+// The two fp16 block scales of this lane half (bytes 2h, 2h+1 of the word)
+// and, for IF4 operands, their INT flags (bits 7 and 15 of f).
+template <int IF4>
+struct Scales {
+  half2_t s[4];
+  uint32_t f[4];
+};
+
+template <int IF4>
+__device__ __forceinline__ void scales16(const Raw &r, uint32_t h, Scales<IF4> &sc) {
 #pragma unroll
-  for (int o = 0; o < 4; ++o) s[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.scale[o] >> (16 * h), 1.0f, false);
+  for (int o = 0; o < 4; ++o) {
+    const uint32_t b = r.scale[o] >> (16 * h);
+    if (IF4) {
+      sc.f[o] = b;
+      sc.s[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b & 0x7F7Fu, 1.0f, false);
+    } else {
+      sc.s[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+    }
+  }
 }
 
 // Dequantize item q = 4 * step + own fragment (0..15) of a chunk into buffer b.
-__device__ __forceinline__ void dequant_item(Stage &st, int b, const Raw &r, const half2_t (&s)[4], uint32_t w,
+template <int IF4>
+__device__ __forceinline__ void dequant_item(Stage &st, int b, const Raw &r, const Scales<IF4> &sc, uint32_t w,
                                              uint32_t lane, int q) {
   const int j = q >> 2, o = q & 3;
   const int frag = o < 2 ? (int)(2 * w) + o : 8 + (int)(2 * w) + (o - 2);
-  st[b][frag][j][lane] = dequant8(r.code[o][j], s[o][j >> 1]);
+  if (IF4) {
+    const bool is_int = (sc.f[o] >> (8 * (j >> 1) + 7)) & 1u;
+    st[b][frag][j][lane] = dequant8_lut(r.code[o][j], sc.s[o][j >> 1], is_int ? kLutIntLo : kLutFpLo,
+                                        is_int ? kLutIntHi : kLutFpHi);
+  } else {
+    st[b][frag][j][lane] = dequant8(r.code[o][j], sc.s[o][j >> 1]);
+  }
 }
 
 struct Ops {
@@ -167,33 +222,34 @@ __device__ __forceinline__ void interleave_step() {
 // publishes it (and retires every read of this chunk's buffer), so step 3
 // can already fetch chunk c+1's first operands.  `rd` is then reloaded with
 // chunk `k_next` (clamped into range by the caller).
+template <int IF4>
 __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Raw &rd, Ops &op, const Panels &p,
                                       uint32_t w, uint32_t wm, uint32_t wn, uint32_t lane,
                                       float16_t (&acc)[4][4]) {
   const int cur = c & 1, nxt = cur ^ 1;
-  half2_t s[4];
-  scales16(rd, p.h, s);
+  Scales<IF4> s;
+  scales16<IF4>(rd, p.h, s);
   Ops nx;
   // step 0
   read_ops(nx, st, cur, wm, wn, lane, 1);
 #pragma unroll
-  for (int q = 0; q < 6; ++q) dequant_item(st, nxt, rd, s, w, lane, q);
+  for (int q = 0; q < 6; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
   mfma16(op, acc);
-  interleave_step<3>();
+  interleave_step<IF4 ? 10 : 3>();
   __builtin_amdgcn_sched_barrier(0);
   // step 1
   read_ops(op, st, cur, wm, wn, lane, 2);
 #pragma unroll
-  for (int q = 6; q < 11; ++q) dequant_item(st, nxt, rd, s, w, lane, q);
+  for (int q = 6; q < 11; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
   mfma16(nx, acc);
-  interleave_step<3>();
+  interleave_step<IF4 ? 10 : 3>();
   __builtin_amdgcn_sched_barrier(0);
   // step 2
   read_ops(nx, st, cur, wm, wn, lane, 3);
 #pragma unroll
-  for (int q = 11; q < 16; ++q) dequant_item(st, nxt, rd, s, w, lane, q);
+  for (int q = 11; q < 16; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
   mfma16(op, acc);
-  interleave_step<3>();
+  interleave_step<IF4 ? 10 : 3>();
   __builtin_amdgcn_sched_barrier(0);
   load_fast(rd, p, k_next);
   __syncthreads();
@@ -204,7 +260,7 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OUT_BF16, int FAST>
+template <int OUT_BF16, int FAST, int IF4>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
   __shared__ Stage st;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -267,10 +323,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
     load_fast(r1, P, min(kChunk, klast));
     __builtin_amdgcn_sched_barrier(0);
     {
-      half2_t s[4];
-      scales16(r0, P.h, s);
+      Scales<IF4> s;
+      scales16<IF4>(r0, P.h, s);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) dequant_item(st, 0, r0, s, w, lane, q);
+      for (int q = 0; q < 16; ++q) dequant_item<IF4>(st, 0, r0, s, w, lane, q);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_fast(r0, P, min(2 * kChunk, klast));
@@ -282,20 +338,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
     // The chunk after the last dequantizes stale codes into the idle buffer.
     uint32_t c = 0;
     for (; c + 1 < nfull; c += 2) {
-      chunk(st, c, min((c + 3) * kChunk, klast), r1, op, P, w, wm, wn, lane, acc);
-      chunk(st, c + 1, min((c + 4) * kChunk, klast), r0, op, P, w, wm, wn, lane, acc);
+      chunk<IF4>(st, c, min((c + 3) * kChunk, klast), r1, op, P, w, wm, wn, lane, acc);
+      chunk<IF4>(st, c + 1, min((c + 4) * kChunk, klast), r0, op, P, w, wm, wn, lane, acc);
     }
-    if (c < nfull) chunk(st, c, klast, r1, op, P, w, wm, wn, lane, acc);
+    if (c < nfull) chunk<IF4>(st, c, klast, r1, op, P, w, wm, wn, lane, acc);
     __syncthreads();  // every wave is done with both buffers before any reuse below
   }
   // remaining K (K % 64 != 0): one chunk at a time through buffer 0
   for (uint32_t k0 = nfull * kChunk; k0 < K; k0 += kChunk) {
     Raw r;
     load_generic(r, P, k0);
-    half2_t s[4];
-    scales16(r, P.h, s);
+    Scales<IF4> s;
+    scales16<IF4>(r, P.h, s);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) dequant_item(st, 0, r, s, w, lane, q);
+    for (int q = 0; q < 16; ++q) dequant_item<IF4>(st, 0, r, s, w, lane, q);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < (int)kSteps; ++j) {
@@ -332,16 +388,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
   }
 }
 
-hipError_t launch_gemm(const GemmParams &p, int out_bf16, hipStream_t s) {
-  const uint32_t tiles = ((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile);
+template <int IF4>
+static void launch_fmt(const GemmParams &p, int out_bf16, uint32_t tiles, hipStream_t s) {
   const bool fast = (p.K % 64) == 0;
   if (out_bf16) {
-    if (fast) hipLaunchKernelGGL((k_gemm<1, 1>), dim3(tiles), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<1, 0>), dim3(tiles), dim3(256), 0, s, p);
+    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(tiles), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(tiles), dim3(256), 0, s, p);
   } else {
-    if (fast) hipLaunchKernelGGL((k_gemm<0, 1>), dim3(tiles), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<0, 0>), dim3(tiles), dim3(256), 0, s, p);
+    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(tiles), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(tiles), dim3(256), 0, s, p);
   }
+}
+
+hipError_t launch_gemm(const GemmParams &p, int out_bf16, int if4, hipStream_t s) {
+  const uint32_t tiles = ((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile);
+  if (if4) launch_fmt<1>(p, out_bf16, tiles, s);
+  else launch_fmt<0>(p, out_bf16, tiles, s);
   return hipGetLastError();
 }
 

@@ -77,6 +77,7 @@ struct GemmParams {
   int64_t ldc;
   uint32_t M, N, K;
 };
-hipError_t launch_gemm(const GemmParams &p, int out_bf16, hipStream_t s);
+// if4: operands may hold IF4 blocks (scale bit 7 = INT flag); 0: NVFP4 only.
+hipError_t launch_gemm(const GemmParams &p, int out_bf16, int if4, hipStream_t s);
 
 }  // namespace nv4

@@ -97,6 +97,29 @@ def test_mlp_step_quantizations(nv, mlp, name):
         assert_rotated_close(g, ref, what=name)
 
 
+def test_weight_8192_if4_gemm(nv):
+    """The 8192^2 IF4 weight as the B operand of a GEMM with a 4096 x 8192
+    activation (IF4 as well), quantized on the GPU and checked bit-exact
+    first; sampled entries of C against the oracle's fp64 GEMM."""
+    import torch
+    wt = synth.weight(8192, 8192, seed=2)
+    x = synth.to_bf16_f32(synth.gaussian(4096, 8192, seed=9))
+    gw = nv.quantize_if4(to_device(wt, "bf16"))
+    gx = nv.quantize_if4(to_device(x, "bf16"))
+    rw = oracle.quantize(wt, fmt=oracle.FMT_IF4)
+    rx = oracle.quantize(x, fmt=oracle.FMT_IF4)
+    assert_bit_exact(q_to_host(gw), rw, "weight if4")
+    assert_bit_exact(q_to_host(gx), rx, "x if4")
+    c = nv.gemm_nvfp4(gx, gw, out_dtype=torch.float32).cpu().numpy()
+    M, N = c.shape
+    rng = np.random.default_rng(11)
+    im = np.concatenate([rng.integers(0, M, 512), [0, M - 1]])
+    in_ = np.concatenate([rng.integers(0, N, 512), [0, N - 1]])
+    ref = oracle.gemm_entries(rx, rw, im, in_, fmt=oracle.FMT_IF4)
+    got = c[im, in_].astype(np.float64)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 1e-5
+
+
 def test_mlp_forward_four_over_six(nv, mlp):
     """The forward pass with Four Over Six scaling of X and W: both operands
     bit-exact at full size, then Y = X W^T on sampled entries."""

@@ -20,11 +20,12 @@ def nv():
     return m
 
 
-def upload(nv, ref):
+def upload(nv, ref, fmt=None):
     import torch
     return nv.QTensor(torch.from_numpy(ref["codes"]).to("cuda:0"),
                       torch.from_numpy(ref["scales"]).to("cuda:0"),
-                      torch.tensor([ref["ts"]], dtype=torch.float32, device="cuda:0"), nv.FORMAT_NVFP4)
+                      torch.tensor([ref["ts"]], dtype=torch.float32, device="cuda:0"),
+                      nv.FORMAT_NVFP4 if fmt is None else fmt)
 
 
 def rel_fro(got, ref):
@@ -98,3 +99,50 @@ def test_gemm_subnormal_and_zero_scales(nv):
         nr = np.linalg.norm(ref[r])
         if nr > 0:
             assert np.linalg.norm(c[r] - ref[r]) <= 1e-5 * nr
+
+
+# ---------------------------------------------------------------- IF4 operands
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 528), (1, 17, 64), (513, 259, 1024),
+                                   (64, 640, 2064)])
+def test_gemm_if4_operands(nv, M, N, K):
+    """IF4 operands (INT-flagged blocks hold integers 0..7): the oracle's fp64
+    GEMM on the same packed operands; also IF4 x NVFP4 (an NVFP4 tensor is an
+    IF4 tensor without flags)."""
+    import torch
+    a = oracle.quantize(synth.weight(M, K, seed=M + K), fmt=oracle.FMT_IF4)
+    b = oracle.quantize(synth.weight(N, K, seed=N + 2 * K), fmt=oracle.FMT_IF4)
+    assert np.any(a["scales"] >= 0x80) and np.any(a["scales"] < 0x80)
+    ref = oracle.gemm_full(a, b, fmt=oracle.FMT_IF4)
+    c = nv.gemm_nvfp4(upload(nv, a, nv.FORMAT_IF4), upload(nv, b, nv.FORMAT_IF4)).cpu().numpy()
+    assert rel_fro(c, ref) <= 1e-3
+    assert rel_fro(c, ref) <= 1e-5
+    bn = oracle.quantize(synth.gaussian(N, K, seed=N + 3 * K))
+    ref = oracle.gemm_full(a, bn, fmt=oracle.FMT_IF4)
+    c = nv.gemm_nvfp4(upload(nv, a, nv.FORMAT_IF4), upload(nv, bn)).cpu().numpy()
+    assert rel_fro(c, ref) <= 1e-5
+    c16 = nv.gemm_nvfp4(upload(nv, a, nv.FORMAT_IF4), upload(nv, bn), out_dtype=torch.bfloat16)
+    c16 = c16.float().cpu().numpy()
+    assert np.all(np.abs(c16 - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+def test_gemm_if4_every_code_and_flag(nv):
+    """Every nibble 0..15 under both flags, with subnormal and normal scales,
+    in one operand; the other operand is a one-hot selector, so each output
+    entry is one dequantized value times a known scale."""
+    K = 256
+    rng = np.random.default_rng(31)
+    codes = rng.integers(0, 256, (64, K // 2), dtype=np.uint8)
+    codes[0, :8] = np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=np.uint8)
+    scales = rng.integers(1, 0x7F, (64, K // 16), dtype=np.uint8)
+    scales[:, ::2] |= 0x80                  # every other block INT-flagged
+    scales[1, :] = np.arange(1, 17) | 0x80   # small (subnormal) scales
+    a = {"codes": codes, "scales": scales, "ts": np.float32(0.75)}
+    eye = np.eye(K, dtype=np.float32)
+    b = oracle.quantize(eye)
+    assert np.all(b["scales"][b["scales"] != 0] == 0x7E)     # the one-hot blocks: 6 x 448
+    ref = oracle.gemm_full(a, b, fmt=oracle.FMT_IF4)
+    c = nv.gemm_nvfp4(upload(nv, a, nv.FORMAT_IF4), upload(nv, b)).cpu().numpy().astype(np.float64)
+    # one exact product per entry; the GPU then rounds twice in fp32 (the
+    # scale product, then the result), the oracle scales in fp64
+    assert np.all(np.abs(c - ref) <= 2.0 ** -22 * np.abs(ref))
+    assert np.array_equal(c == 0, ref == 0)
