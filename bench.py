@@ -340,8 +340,9 @@ def main():
 
 def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
     """Options beyond the step, timed on the same inputs and buffers (not part
-    of `value`): IF4 quantization of X and W and the Y GEMM on IF4 operands;
-    Four Over Six forward scaling of X and W."""
+    of `value`): dY quantized along both axes from one read; IF4 quantization
+    of X and W and the Y GEMM on IF4 operands; Four Over Six forward scaling
+    of X and W."""
     def timed(fn):
         fn()
         torch.cuda.synchronize()
@@ -357,6 +358,18 @@ def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
         return total / reps
 
     res = {}
+    # dY along both axes from one read (the step quantizes it twice)
+    qr, qc = outs["qdYr"], outs["qdYc"]
+    wsd = torch.empty(nv.workspace_size_dual(dY.shape[0], dY.shape[1]), dtype=torch.uint8, device=dY.device)
+    ms = timed(lambda: nv.quantize_nvfp4_dual(dY, rht_signs=signs, seed=1004, stream_id=0, out_rows=qr,
+                                              out_cols=qc, workspace=wsd))
+    alg = dY.numel() * (2.0 + 2 * 0.5625)
+    res["dY_dual_axis"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                           "bytes_per_elem": 3.125, "shape_in": list(dY.shape),
+                           "what": "RHT + MS-EDEN of dY along rows and columns from one read "
+                                   "(input once, two sets of codes and scales)"}
+    del wsd
     # IF4 forward operands (the output buffers of the step are reused), then
     # the Y GEMM on them through the INT-flag-aware entry point
     qa = nv.quantize_if4(X, out=outs["qX"], workspace=wss["qX"])

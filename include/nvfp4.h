@@ -158,6 +158,28 @@ int nvfp4_quantize_nvfp4(const void *x, int in_dtype, int64_t rows, int64_t cols
                          float *tensor_scale, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * MS-EDEN of one tensor along both axes from a single read of it: the
+ * backward pass re-quantizes the output gradient row-wise (for the input
+ * gradient) and along its reduction dimension (for the weight gradient)
+ * [QII-sum "Quantisierung im Rueckwaertsdurchlauf"].  The results are those
+ * of two nvfp4_quantize_nvfp4 calls with these options and axis 0 (codes_r,
+ * scales_r, ts_r: [rows x cols/2], [rows x cols/16]) and axis 1 (codes_c,
+ * scales_c, ts_c: [cols x rows/2], [cols x rows/16]); o->axis is ignored,
+ * o->rounding must be NVFP4_MSEDEN, and each output has its own tensor scale
+ * (both equal *o->tensor_scale_in when it is given).  Both axes must meet the
+ * shape rules (multiples of 16, of 128 with rotation or group 128) and x the
+ * axis-0 alignment.  ws: at least nvfp4_workspace_size_dual() bytes,
+ * 256-byte aligned.
+ */
+int nvfp4_quantize_nvfp4_dual(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                              const nvfp4_opts *o, uint8_t *codes_r, uint8_t *scales_r, float *ts_r,
+                              uint8_t *codes_c, uint8_t *scales_c, float *ts_c, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* Workspace bytes of nvfp4_quantize_nvfp4_dual (both axes' workspaces). */
+size_t nvfp4_workspace_size_dual(int64_t rows, int64_t cols, const nvfp4_opts *o);
+
+/*
  * IF4 quantization [IF4 abstract, Figure 1, Figure 3]: every 16-group is
  * quantized as NVFP4 (E2M1 under scale a/6) and as scaled INT4 (integers
  * 0..7 under its own scale a/7, both RNE), and keeps the one with the

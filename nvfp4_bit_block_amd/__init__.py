@@ -18,6 +18,7 @@ __all__ = [
     "RTN", "SR", "MSEDEN", "FORMAT_NVFP4", "FORMAT_IF4", "QTensor", "NvFp4Error",
     "lib", "signs_to_words", "workspace_size", "quantize_nvfp4", "quantize_if4",
     "dequantize", "gemm_nvfp4", "rht", "abi_version", "SCALE_MAX6", "SCALE_4OVER6",
+    "quantize_nvfp4_dual", "workspace_size_dual",
 ]
 
 RTN, SR, MSEDEN = 0, 1, 2
@@ -69,6 +70,11 @@ def lib():
     L.nvfp4_opts_init.argtypes = [ctypes.POINTER(_Opts)]
     L.nvfp4_workspace_size.restype = SZ
     L.nvfp4_workspace_size.argtypes = [I64, I64, ctypes.POINTER(_Opts)]
+    L.nvfp4_workspace_size_dual.restype = SZ
+    L.nvfp4_workspace_size_dual.argtypes = [I64, I64, ctypes.POINTER(_Opts)]
+    L.nvfp4_quantize_nvfp4_dual.restype = INT
+    L.nvfp4_quantize_nvfp4_dual.argtypes = [P, INT, I64, I64, I64, ctypes.POINTER(_Opts), P, P, P, P, P, P,
+                                            P, SZ, P]
     for name in ("nvfp4_quantize_nvfp4", "nvfp4_quantize_if4"):
         f = getattr(L, name)
         f.restype = INT
@@ -212,6 +218,46 @@ def quantize_nvfp4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0,
     selects Four Over Six block scaling (RTN only).  Returns a QTensor."""
     return _quantize(lib().nvfp4_quantize_nvfp4, x, rounding, axis, rht_signs, seed, stream_id,
                      eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4, scale_rule)
+
+
+def quantize_nvfp4_dual(x, rht_signs=None, seed=0, stream_id=0, eden_group=128, tensor_scale_in=None,
+                        out_rows=None, out_cols=None, workspace=None):
+    """MS-EDEN of a 2-D device tensor along both axes from one read (see
+    ``nvfp4_quantize_nvfp4_dual``): returns (row-wise QTensor [rows, cols],
+    column-wise QTensor [cols, rows]), equal to two quantize_nvfp4 calls with
+    rounding "mseden" and axis 0 / axis 1."""
+    import torch
+    L = lib()
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise NvFp4Error("x must be a 2-D device tensor with unit stride along its last dimension")
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else cols
+    o = _opts(MSEDEN, 0, rht_signs, seed, stream_id, eden_group, tensor_scale_in)
+    dev = x.device
+
+    def alloc(R, K):
+        return QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                       torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
+                       torch.empty(1, dtype=torch.float32, device=dev), FORMAT_NVFP4)
+    qr = out_rows if out_rows is not None else alloc(rows, cols)
+    qc = out_cols if out_cols is not None else alloc(cols, rows)
+    wsz = int(L.nvfp4_workspace_size_dual(rows, cols, ctypes.byref(o)))
+    if workspace is None or workspace.numel() < wsz:
+        workspace = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+    rc = L.nvfp4_quantize_nvfp4_dual(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld,
+                                     ctypes.byref(o), ctypes.c_void_p(qr.codes.data_ptr()),
+                                     ctypes.c_void_p(qr.scales.data_ptr()),
+                                     ctypes.c_void_p(qr.tensor_scale.data_ptr()),
+                                     ctypes.c_void_p(qc.codes.data_ptr()), ctypes.c_void_p(qc.scales.data_ptr()),
+                                     ctypes.c_void_p(qc.tensor_scale.data_ptr()),
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(torch))
+    _check(rc)
+    return qr, qc
+
+
+def workspace_size_dual(rows, cols, eden_group=128, tensor_scale_in=None):
+    o = _opts(MSEDEN, 0, None, 0, 0, eden_group, tensor_scale_in)
+    return int(lib().nvfp4_workspace_size_dual(int(rows), int(cols), ctypes.byref(o)))
 
 
 def quantize_if4(x, axis=0, rht_signs=None, tensor_scale_in=None, out=None, workspace=None):

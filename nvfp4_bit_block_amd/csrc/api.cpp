@@ -202,6 +202,48 @@ int quantize_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, int64
   return ok();
 }
 
+int quantize_dual_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                       const nvfp4_opts *o, uint8_t *codes_r, uint8_t *scales_r, float *ts_r,
+                       uint8_t *codes_c, uint8_t *scales_c, float *ts_c, void *ws, size_t ws_bytes,
+                       void *stream) {
+  if (!o) return fail(NVFP4_INVALID_ARG, "opts is NULL");
+  if (o->rounding != NVFP4_MSEDEN)
+    return fail(NVFP4_INVALID_ARG, "the two-axis quantization takes rounding MSEDEN only");
+  nvfp4_opts orow = *o, ocol = *o;
+  orow.axis = 0;
+  ocol.axis = 1;
+  Shape shr, shc;
+  int st = check_input(x, in_dtype, rows, cols, ld, &orow, false, &shr);
+  if (!st) st = check_input(x, in_dtype, rows, cols, ld, &ocol, false, &shc);
+  if (st) return st;
+  const size_t wr = nvfp4_workspace_size(rows, cols, &orow);
+  if (ws_bytes < wr) return fail(NVFP4_WS_TOO_SMALL, "workspace of %zu bytes is below the %zu required",
+                                 ws_bytes, nvfp4_workspace_size_dual(rows, cols, o));
+  void *ws_c = ws ? static_cast<char *>(ws) + wr : nullptr;
+  st = check_outputs(rows, cols, &orow, shr, codes_r, scales_r, ts_r, ws, wr);
+  if (!st) st = check_outputs(rows, cols, &ocol, shc, codes_c, scales_c, ts_c, ws_c, ws_bytes - wr);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (shr.nblocks == 0) {
+    st = write_trivial_scale(o, ts_r, s);
+    return st ? st : write_trivial_scale(o, ts_c, s);
+  }
+  QuantParams pr, pc;
+  fill_common(pr, x, in_dtype, rows, cols, ld, &orow, shr, codes_r, scales_r, ts_r, ws);
+  fill_common(pc, x, in_dtype, rows, cols, ld, &ocol, shc, codes_c, scales_c, ts_c, ws_c);
+  const int bf = in_dtype == NVFP4_BF16;
+  const uint32_t grid = dual_grid(pr, bf);
+  hipError_t e = launch_quant_dual(pr, pc, bf, o->tensor_scale_in != nullptr, grid, s);
+  if (e == hipSuccess && !o->tensor_scale_in) {
+    pr.npartial = grid;
+    pc.npartial = grid;
+    e = launch_eden_scales(pr, eden_scales_grid(pr), s);
+    if (e == hipSuccess) e = launch_eden_scales(pc, eden_scales_grid(pc), s);
+  }
+  if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,6 +264,23 @@ size_t nvfp4_workspace_size(int64_t rows, int64_t cols, const nvfp4_opts *o) {
     bytes += (size_t)R * (size_t)(K / 16) * sizeof(float);
   }
   return round_up(bytes, 256);
+}
+
+size_t nvfp4_workspace_size_dual(int64_t rows, int64_t cols, const nvfp4_opts *o) {
+  if (!o) return 0;
+  nvfp4_opts orow = *o, ocol = *o;
+  orow.axis = 0;
+  ocol.axis = 1;
+  const size_t a = nvfp4_workspace_size(rows, cols, &orow), b = nvfp4_workspace_size(rows, cols, &ocol);
+  return (a && b) ? a + b : 0;
+}
+
+int nvfp4_quantize_nvfp4_dual(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                              const nvfp4_opts *o, uint8_t *codes_r, uint8_t *scales_r, float *ts_r,
+                              uint8_t *codes_c, uint8_t *scales_c, float *ts_c, void *ws,
+                              size_t ws_bytes, void *stream) {
+  return quantize_dual_impl(x, in_dtype, rows, cols, ld, o, codes_r, scales_r, ts_r, codes_c, scales_c,
+                            ts_c, ws, ws_bytes, stream);
 }
 
 int nvfp4_quantize_nvfp4(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,

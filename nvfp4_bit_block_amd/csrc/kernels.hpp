@@ -54,6 +54,10 @@ struct QuantParams {
 hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, uint32_t grid,
                         hipStream_t s);
 hipError_t launch_eden_scales(const QuantParams &p, uint32_t grid, hipStream_t s);
+// MS-EDEN along both axes from one read (fused = given tensor scales).
+hipError_t launch_quant_dual(const QuantParams &pr, const QuantParams &pc, int in_bf16, int fused,
+                             uint32_t grid, hipStream_t s);
+uint32_t dual_grid(const QuantParams &pr, int in_bf16);
 uint32_t quant_grid(const QuantParams &p, int in_bf16, int axis);
 uint32_t eden_scales_grid(const QuantParams &p);
 

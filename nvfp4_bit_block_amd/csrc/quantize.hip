@@ -317,10 +317,64 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
 // Each load instruction reads 8 rows x 128 contiguous bytes; no LDS is used.
 // The rotation sign of a position is the same for every column, so it is
 // XORed into each raw row word once.
+// One wave's column tile (tile row tt, tile column tc): 128 positions along
+// the reduction x TCOL columns; see k_quant_cols.
 template <int IN_BF16, int MODE>
-__global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
+__device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint32_t tc, uint32_t lig, uint32_t q,
+                                         uint32_t sbits, float s_t, float &lmax) {
   constexpr int CPL = IN_BF16 ? 8 : 4;  // columns per 16-byte chunk
   constexpr int TCOL = 8 * CPL;         // columns per wave tile
+  const uint32_t row0 = tt * 128 + 16 * lig;     // this lane's 16 rows
+  const uint32_t col0 = tc * TCOL + CPL * q;     // this lane's CPL columns
+  const bool rows_ok = row0 < p.rows;            // rows % 16 == 0: whole slab or nothing
+  uint32_t w[16][4];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0u;
+    if (rows_ok && col0 < p.cols) {
+      const size_t off = (size_t)(row0 + r) * p.ld + col0;
+      if (p.vec && col0 + CPL <= p.cols) {
+        const uint4 a = IN_BF16 ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off)
+                                : *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.x) + off);
+        w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+      } else if (IN_BF16) {  // (fully unrolled: a runtime index would put w in scratch)
+        const uint16_t *src = static_cast<const uint16_t *>(p.x) + off;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          if (col0 + j < p.cols) w[r][j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
+      } else {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const float *>(p.x) + off);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          if (col0 + j < p.cols) w[r][j] = src[j];
+      }
+    }
+    const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[r][c] ^= sflip;
+  }
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    float z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (IN_BF16) {
+        const uint32_t v = w[r][j >> 1];
+        z[r] = (j & 1) ? bf16_hi(v) : bf16_lo(v);
+      } else {
+        z[r] = __uint_as_float(w[r][j]);
+      }
+    }
+    if (p.rht) fwht128_group(z, lig);
+    const uint32_t col = col0 + j;
+    const uint32_t kblk = tt * 8 + lig;
+    const bool active = rows_ok && col < p.cols;
+    quant_block<MODE>(z, active ? col * p.K16 + kblk : 0u, active, p, s_t, lmax);
+  }
+}
+
+template <int IN_BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
   if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kEdenFused) {
@@ -337,57 +391,71 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   for (uint32_t t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6); t < p.ntiles; t += waves) {
     const uint32_t tt = fdiv(t, p.ctiles_div);
     const uint32_t tc = t - tt * nct;
-    const uint32_t row0 = tt * 128 + 16 * lig;     // this lane's 16 rows
-    const uint32_t col0 = tc * TCOL + CPL * q;     // this lane's CPL columns
-    const bool rows_ok = row0 < p.rows;            // rows % 16 == 0: whole slab or nothing
-    uint32_t w[16][4];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0u;
-      if (rows_ok && col0 < p.cols) {
-        const size_t off = (size_t)(row0 + r) * p.ld + col0;
-        if (p.vec && col0 + CPL <= p.cols) {
-          const uint4 a = IN_BF16 ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off)
-                                  : *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.x) + off);
-          w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
-        } else if (IN_BF16) {  // (fully unrolled: a runtime index would put w in scratch)
-          const uint16_t *src = static_cast<const uint16_t *>(p.x) + off;
-#pragma unroll
-          for (int j = 0; j < CPL; ++j)
-            if (col0 + j < p.cols) w[r][j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
-        } else {
-          const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const float *>(p.x) + off);
-#pragma unroll
-          for (int j = 0; j < CPL; ++j)
-            if (col0 + j < p.cols) w[r][j] = src[j];
-        }
-      }
-      const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[r][c] ^= sflip;
-    }
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      float z[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (IN_BF16) {
-          const uint32_t v = w[r][j >> 1];
-          z[r] = (j & 1) ? bf16_hi(v) : bf16_lo(v);
-        } else {
-          z[r] = __uint_as_float(w[r][j]);
-        }
-      }
-      if (p.rht) fwht128_group(z, lig);
-      const uint32_t col = col0 + j;
-      const uint32_t kblk = tt * 8 + lig;
-      const bool active = rows_ok && col < p.cols;
-      quant_block<MODE>(z, active ? col * p.K16 + kblk : 0u, active, p, s_t, lmax);
-    }
+    col_tile<IN_BF16, MODE>(p, tt, tc, lig, q, sbits, s_t, lmax);
   }
   if constexpr (MODE == kAmax || MODE == kEden) {
     const float m = block_max(lmax, red, kThreads);
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
+  }
+}
+
+// ---------------------------------------------------------------- both axes
+// MS-EDEN of one tensor along both axes from one read of it (the backward
+// pass re-quantizes the output gradient along its rows and along its
+// reduction dimension).  A workgroup takes a tile of 128 rows x 4 wave tiles
+// of columns: the row-wise pass codes its 128-element row groups, then each
+// wave codes its column tile of the same rows, re-reading the tile from L2.
+// pr / pc: the row-wise (axis 0) and column-wise (axis 1) outputs; each gets
+// its own partial maxima and target scales.
+template <int IN_BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantParams pc) {
+  constexpr int CPL = IN_BF16 ? 8 : 4;
+  constexpr int TCOL = 8 * CPL;
+  constexpr uint32_t kWidth = 4 * TCOL;      // tile columns
+  constexpr uint32_t kBpr = kWidth / 16;     // row blocks per tile row
+  __shared__ float red[kThreads / kWave];
+  float s_r = 1.0f, s_c = 1.0f;
+  if constexpr (MODE == kEdenFused) {
+    s_r = *pr.ts_in;
+    s_c = *pc.ts_in;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *pr.ts_out = s_r;
+      *pc.ts_out = s_c;
+    }
+  }
+  const uint32_t lane = threadIdx.x & 63u, lig = group_pos(lane);
+  const uint32_t rank = (threadIdx.x & ~63u) + lane_block_rank(lane);
+  const uint32_t q = ((lane >> 2) & 1u) | ((lane >> 4) << 1);
+  const uint32_t sbits = pc.rht ? lane_sign_bits(pc.sg, lig) : 0u;
+  const SignMasks sm = make_masks<IN_BF16>(pr, lig);
+  const uint32_t ntc = (pr.cols + kWidth - 1) / kWidth;   // tile columns
+  const uint32_t ntiles = (pr.rows / 128) * ntc;
+  float lmax_r = 0.0f, lmax_c = 0.0f;
+  for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const uint32_t tt = t / ntc, tcw = t - tt * ntc;
+    // row-wise: 128 x kBpr blocks, rotation groups of 8 consecutive blocks
+#pragma unroll 1
+    for (uint32_t i = 0; i < 128 * kBpr / kThreads; ++i) {
+      const uint32_t bt = i * kThreads + rank;
+      const uint32_t row = tt * 128 + bt / kBpr;
+      const uint32_t kb = tcw * kBpr + bt % kBpr;
+      const bool active = kb < pr.K16;
+      const uint32_t gb = row * pr.K16 + kb;
+      RawBlock<IN_BF16> raw = {};
+      if (active) load_row_block<IN_BF16>(pr, gb, raw);
+      float z[16];
+      unpack_block<IN_BF16>(raw, sm, z);
+      if (pr.rht) fwht128_group(z, lig);
+      quant_block<MODE>(z, active ? gb : 0u, active, pr, s_r, lmax_r);
+    }
+    // column-wise: wave w takes wave tile column 4 * tcw + w
+    col_tile<IN_BF16, MODE>(pc, tt, 4 * tcw + (threadIdx.x >> 6), lig, q, sbits, s_c, lmax_c);
+  }
+  if constexpr (MODE == kEden) {
+    const float mr = block_max(lmax_r, red, kThreads);
+    if (threadIdx.x == 0) pr.partial[blockIdx.x] = mr;
+    const float mc = block_max(lmax_c, red, kThreads);
+    if (threadIdx.x == 0) pc.partial[blockIdx.x] = mc;
   }
 }
 
@@ -474,6 +542,25 @@ hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, 
     launch_mode<1>(p, axis, mode, grid, s);
   else
     launch_mode<0>(p, axis, mode, grid, s);
+  return hipGetLastError();
+}
+
+uint32_t dual_grid(const QuantParams &pr, int in_bf16) {
+  const uint32_t width = in_bf16 ? 256u : 128u;
+  const uint64_t tiles = (uint64_t)(pr.rows / 128) * ((pr.cols + width - 1) / width);
+  uint64_t g = tiles < 1 ? 1 : tiles;
+  return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);
+}
+
+hipError_t launch_quant_dual(const QuantParams &pr, const QuantParams &pc, int in_bf16, int fused,
+                             uint32_t grid, hipStream_t s) {
+  if (in_bf16) {
+    if (fused) hipLaunchKernelGGL((k_quant_dual<1, kEdenFused>), dim3(grid), dim3(kThreads), 0, s, pr, pc);
+    else hipLaunchKernelGGL((k_quant_dual<1, kEden>), dim3(grid), dim3(kThreads), 0, s, pr, pc);
+  } else {
+    if (fused) hipLaunchKernelGGL((k_quant_dual<0, kEdenFused>), dim3(grid), dim3(kThreads), 0, s, pr, pc);
+    else hipLaunchKernelGGL((k_quant_dual<0, kEden>), dim3(grid), dim3(kThreads), 0, s, pr, pc);
+  }
   return hipGetLastError();
 }
 

@@ -107,6 +107,25 @@ def test_quantize_rejections(nv):
     assert b"multiple of 16" in L.nvfp4_last_error()
 
 
+def test_dual_rejections_and_workspace(nv):
+    L = nv.lib()
+    P = ctypes.c_void_p
+    o = _opts(nv, rounding=2)
+    w0 = L.nvfp4_workspace_size(128, 256, ctypes.byref(_opts(nv, rounding=2)))
+    w1 = L.nvfp4_workspace_size(128, 256, ctypes.byref(_opts(nv, rounding=2, axis=1)))
+    assert L.nvfp4_workspace_size_dual(128, 256, ctypes.byref(o)) == w0 + w1
+
+    def d(rows=128, cols=256, ws_bytes=1 << 30, **kw):
+        oo = _opts(nv, **({"rounding": 2} | kw))
+        return L.nvfp4_quantize_nvfp4_dual(P(FAKE), 1, rows, cols, cols, ctypes.byref(oo), P(FAKE), P(FAKE),
+                                           P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), ws_bytes, None)
+    assert d(rounding=0) == INVALID                  # MS-EDEN only
+    assert d(rows=100) == SHAPE                      # the column-wise K = rows
+    assert d(cols=200) == SHAPE
+    assert d(rows=144) == SHAPE                      # group 128 along the rows
+    assert d(ws_bytes=w0) == WS_SMALL
+
+
 def test_dequantize_and_gemm_rejections(nv):
     L = nv.lib()
     P = ctypes.c_void_p

@@ -120,6 +120,17 @@ def test_weight_8192_if4_gemm(nv):
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 1e-5
 
 
+def test_mlp_dy_dual_axis(nv, mlp):
+    """dY of the MLP step quantized along both axes from one read: the same
+    outputs as the oracle's row-wise and column-wise RHT + MS-EDEN."""
+    _, _, dy, signs = mlp
+    w = oracle.signs_words(signs)
+    qr, qc = nv.quantize_nvfp4_dual(to_device(dy, "bf16"), rht_signs=signs, seed=7, stream_id=3)
+    for axis, q in ((0, qr), (1, qc)):
+        ref = oracle.quantize(dy, rounding=oracle.MSEDEN, axis=axis, rht_on=True, signs_w=w, seed=7, stream=3)
+        assert_rotated_close(q_to_host(q), ref, what=f"dY dual axis{axis}")
+
+
 def test_mlp_forward_four_over_six(nv, mlp):
     """The forward pass with Four Over Six scaling of X and W: both operands
     bit-exact at full size, then Y = X W^T on sampled entries."""

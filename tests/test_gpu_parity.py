@@ -127,6 +127,44 @@ def test_four_over_six_rotation_and_given_scale(nv, axis):
     assert_bit_exact(g, ref, f"4over6 given scale axis{axis}")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("group,rot", [(128, True), (16, True), (128, False), (16, False)])
+def test_dual_axis_mseden(nv, dtype, group, rot):
+    """MS-EDEN along both axes from one read equals the oracle's axis-0 and
+    axis-1 quantizations (and the two separate GPU calls, bit for bit);
+    shapes with a partial column tile."""
+    rng = np.random.default_rng(19)
+    signs = synth.signs_from_rng(rng) if rot else None
+    w = None if signs is None else oracle.signs_words(signs)
+    for i, (r, c) in enumerate([(256, 384), (128, 128), (384, 1152)]):
+        x = synth.gradient(r, c, seed=600 + i)[0] if dtype == "bf16" else synth.gaussian(r, c, seed=600 + i)
+        xt = to_device(x, dtype)
+        qr, qc = nv.quantize_nvfp4_dual(xt, rht_signs=signs, seed=3, stream_id=2, eden_group=group)
+        gr, gc = q_to_host(qr), q_to_host(qc)
+        for axis, g in ((0, gr), (1, gc)):
+            ref = oracle.quantize(x, rounding=oracle.MSEDEN, axis=axis, rht_on=rot, signs_w=w, seed=3,
+                                  stream=2, eden_group=group)
+            what = f"dual {dtype} g{group} rot{rot} axis{axis} {r}x{c}"
+            if rot:
+                assert_rotated_close(g, ref, what=what)
+            else:
+                assert_bit_exact(g, ref, what)
+            sep = q_to_host(nv.quantize_nvfp4(xt, rounding="mseden", axis=axis, rht_signs=signs, seed=3,
+                                              stream_id=2, eden_group=group))
+            assert_bit_exact(g, sep, what + " vs separate call")
+
+
+def test_dual_axis_given_scale(nv):
+    import torch
+    x = synth.gradient(256, 256, seed=610)[0]
+    ts = np.float32(2.5e-3)
+    qr, qc = nv.quantize_nvfp4_dual(to_device(x, "bf16"), tensor_scale_in=torch.tensor([ts], device="cuda:0"),
+                                    seed=4)
+    for axis, q in ((0, qr), (1, qc)):
+        ref = oracle.quantize(x, rounding=oracle.MSEDEN, axis=axis, ts_in=float(ts), seed=4)
+        assert_bit_exact(q_to_host(q), ref, f"dual given scale axis{axis}")
+
+
 @pytest.mark.parametrize("axis", [0, 1])
 def test_rht_values(nv, axis):
     import torch
