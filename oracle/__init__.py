@@ -15,7 +15,7 @@ import numpy as np
 
 from . import build as _build
 
-FMT_NVFP4, FMT_IF4, FMT_NVINT4, FMT_NVFP4_4OVER6 = 0, 1, 2, 3
+FMT_NVFP4, FMT_IF4, FMT_NVINT4, FMT_NVFP4_4OVER6, FMT_NVFP4_SEARCH = 0, 1, 2, 3, 4
 RTN, SR, MSEDEN = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -376,6 +376,60 @@ static void fos_block(const float *z, float s_t, uint8_t *codes_row, int64_t k0,
   for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, use4 ? n4[i] : n6[i]);
 }
 
+/* Scale search, RTN with a searched block scale: the standard NVFP4 scale
+ * (block maximum mapped to 6) is not the error-minimizing one; a search over
+ * nearby scale values lowers the error [PAL section "The two corners, and
+ * what the palette does to them": the low-error corner sweeps 19 candidate
+ * scales per block, rounds to nearest and keeps the best, values above the
+ * top level clipping; the ScaleSearch abstract among the IF4 page's related
+ * papers: a fine-grained search over the scale's mantissa bits, 27 % lower
+ * NVFP4 error].
+ * READING: the candidates are the 19 E4M3 scale bytes e0-9 .. e0+9 around the
+ * RNE byte e0 of (a/6)/s_t, visited nearest first (e0, e0-1, e0+1, ...) and
+ * skipping bytes outside 1..126 (e0 itself is always tried); codes by RTN at
+ * each candidate (magnitudes clamped to 6); the block keeps the first
+ * candidate with a strictly smaller pairwise sum of squared errors.  The
+ * tensor scale is NVFP4's amax / (6 x 448).  The study's least-squares
+ * reconstruction scale is not applied: with E4M3 scales and codes re-rounded
+ * at every candidate, the searched minimum already is the best E4M3 scale
+ * for its codes within the window.
+ * Pinned by: the 27 % error reduction against NVFP4 RTN on N(0,1) data; the
+ * kept candidate is the float64 brute-force minimum over the window; never
+ * worse than RTN per block. */
+static void search_block(const float *z, float s_t, uint8_t *codes_row, int64_t k0,
+                         uint8_t *scale_out) {
+  float a = 0.0f;
+  for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(z[i]));
+  const int e0 = orc_e4m3_rne_sat((a / 6.0f) / s_t);
+  int best_e = -1, best_nib[16];
+  float best_sse = 0.0f;
+  for (int t = 0; t < 19; t++) {
+    const int d = (t + 1) / 2 * ((t & 1) ? -1 : 1);   /* 0, -1, +1, -2, +2, ... */
+    const int e = e0 + d;
+    if (t > 0 && (e < 1 || e > 126)) continue;
+    const float S = orc_e4m3_value(e) * s_t;
+    const float r = (e != 0) ? 1.0f / S : 0.0f;
+    int nib[16];
+    float sq[16];
+    for (int i = 0; i < 16; i++) {
+      int mag = (e != 0) ? orc_e2m1_rne(fminf(fabsf(z[i] * r), 6.0f)) : 0;
+      float val = GRID_E2M1[mag];
+      if (signbit(z[i])) val = -val;
+      float dd = z[i] - val * S;
+      sq[i] = dd * dd;
+      nib[i] = (signbit(z[i]) ? 8 : 0) | mag;
+    }
+    const float sse = orc_pairwise_sum(sq, 16);
+    if (best_e < 0 || sse < best_sse) {
+      best_e = e;
+      best_sse = sse;
+      memcpy(best_nib, nib, sizeof(nib));
+    }
+  }
+  *scale_out = (uint8_t)best_e;
+  for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, best_nib[i]);
+}
+
 /* MS-EDEN, first half, for one correction group of G elements (G = 128, the
  * rotation group, or 16) [QII-abs; QII-sum "Kerninnovationen" and
  * "Quantisierung im Rueckwaertsdurchlauf"]: the randomness moves from the
@@ -439,7 +493,7 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
                  uint8_t *codes, uint8_t *scales, float *ts_out,
                  float *z_out, float *tb_out) {
   if (!x || !codes || !scales || !ts_out) return ORC_BAD_ARG;
-  if (format < 0 || format > 3 || rounding < 0 || rounding > 2 || axis < 0 || axis > 1)
+  if (format < 0 || format > 4 || rounding < 0 || rounding > 2 || axis < 0 || axis > 1)
     return ORC_BAD_ARG;
   if (format != ORC_FMT_NVFP4 && rounding != ORC_RTN) return ORC_BAD_ARG;
   if (rows < 0 || cols < 0 || ld < cols) return ORC_BAD_SHAPE;
@@ -498,6 +552,8 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
                       k, sc);
         else if (format == ORC_FMT_NVFP4_4OVER6)
           fos_block(zb, s_t, codes + r * (K / 2), k, sc);
+        else if (format == ORC_FMT_NVFP4_SEARCH)
+          search_block(zb, s_t, codes + r * (K / 2), k, sc);
         else
           if4_block(zb, s_t, format, codes + r * (K / 2), k, sc);
       }

@@ -23,7 +23,8 @@ extern "C" {
 
 /* element formats */
 enum { ORC_FMT_NVFP4 = 0, ORC_FMT_IF4 = 1, ORC_FMT_NVINT4 = 2,
-       ORC_FMT_NVFP4_4OVER6 = 3 /* NVFP4 codes, block maximum mapped to 6 or 4 */ };
+       ORC_FMT_NVFP4_4OVER6 = 3, /* NVFP4 codes, block maximum mapped to 6 or 4   */
+       ORC_FMT_NVFP4_SEARCH = 4  /* NVFP4 codes, block scale searched (19 E4M3)   */ };
 /* rounding of the E2M1 codes (and, for MS-EDEN, of the block scale) */
 enum { ORC_RTN = 0, ORC_SR = 1, ORC_MSEDEN = 2 };
 

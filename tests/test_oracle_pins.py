@@ -326,6 +326,54 @@ def test_four_over_six_never_worse_than_rtn_at_same_scale(orc):
     assert e46.sum() < e6.sum()
 
 
+def test_scale_search_lowers_nvfp4_error_by_27_percent(orc):
+    """ScaleSearch abstract (among the IF4 page's related papers): searching
+    the block scale over its mantissa steps lowers NVFP4's quantization error
+    by 27 %.  On N(0,1) data the 19-candidate search gives 27.1 % (27.09-27.12
+    over four 4096^2 samples); tolerance half a unit of the printed digit."""
+    x = synth.gaussian(2048, 2048, seed=0)
+    r = orc.quantize(x)
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4_SEARCH)
+    assert q["ts"] == r["ts"]
+    dr = orc.dequantize(r["codes"], r["scales"], r["ts"]).astype(np.float64)
+    dq = orc.dequantize(q["codes"], q["scales"], q["ts"]).astype(np.float64)
+    red = 100.0 * (1.0 - np.mean((dq - x) ** 2) / np.mean((dr - x) ** 2))
+    assert 26.5 <= red <= 27.5, red
+
+
+def test_scale_search_keeps_the_window_minimum(orc):
+    """Per block the kept scale is the float64 brute-force minimum over the
+    19 E4M3 bytes around the RTN byte (codes elementwise nearest at each),
+    never worse than RTN; near-ties are left to the fp32 decision."""
+    x = synth.gradient(32, 512, seed=24)[0]
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4_SEARCH)
+    r = orc.quantize(x)
+    ts = float(q["ts"])
+    e4 = np.array([orc.e4m3_value(b) for b in range(127)], dtype=np.float64)
+    grid = np.array([orc.e2m1_value(c) for c in range(8)], dtype=np.float64)
+    moved = 0
+    for row in range(x.shape[0]):
+        for b in range(x.shape[1] // 16):
+            z = x[row, 16 * b:16 * b + 16].astype(np.float64)
+            e0 = int(r["scales"][row, b])
+            errs = {}
+            for e in range(max(e0 - 9, 1), min(e0 + 9, 126) + 1):
+                S = e4[e] * np.float64(np.float32(ts))
+                y = np.minimum(np.abs(z) / S, 6.0)
+                rec = np.sign(z) * grid[np.argmin(np.abs(y[:, None] - grid[None, :]), axis=1)] * S
+                errs[e] = ((z - rec) ** 2).sum()
+            got = int(q["scales"][row, b])
+            assert abs(got - e0) <= 9
+            best = min(errs.values())
+            if e0 >= 1:
+                assert errs[got] <= errs[e0] * (1 + 1e-6) + 1e-30
+            srt = sorted(errs.values())
+            if len(srt) > 1 and srt[1] - srt[0] > 1e-3 * srt[0]:
+                assert errs[got] == best
+            moved += int(got != e0)
+    assert moved > 0
+
+
 def test_if4_int_flag_only_in_if4(orc):
     x = synth.weight(16, 128, seed=13)
     assert np.all(orc.quantize(x)["scales"] < 0x80)
