@@ -341,8 +341,8 @@ def main():
 def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
     """Options beyond the step, timed on the same inputs and buffers (not part
     of `value`): dY quantized along both axes from one read; IF4 quantization
-    of X and W and the Y GEMM on IF4 operands; Four Over Six forward scaling
-    of X and W."""
+    of X and W and the Y GEMM on IF4 operands; Four Over Six and searched
+    block scales for X and W."""
     def timed(fn):
         fn()
         torch.cuda.synchronize()
@@ -386,11 +386,13 @@ def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
         res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
                      "shape_in": list(x.shape), "what": "IF4 (FP4/INT4 per 16-group), axis 0"}
     del Yb
-    for name, x, q in (("X_4over6", X, "qX"), ("W_4over6", W, "qW")):
-        ms = timed(lambda: nv.quantize_nvfp4(x, scale_rule="4over6", out=outs[q], workspace=wss[q]))
-        gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
-        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                     "shape_in": list(x.shape), "what": "RTN, Four Over Six block scaling, axis 0"}
+    for rule, what in (("4over6", "RTN, Four Over Six block scaling, axis 0"),
+                       ("search", "RTN, block scale searched over 19 E4M3 bytes, axis 0")):
+        for name, x, q in (("X_" + rule, X, "qX"), ("W_" + rule, W, "qW")):
+            ms = timed(lambda: nv.quantize_nvfp4(x, scale_rule=rule, out=outs[q], workspace=wss[q]))
+            gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
+            res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                         "shape_in": list(x.shape), "what": what}
     return res
 
 

@@ -90,8 +90,10 @@ typedef enum nvfp4_format { NVFP4_FORMAT_NVFP4 = 0, NVFP4_FORMAT_IF4 = 1 } nvfp4
 /* How an RTN block scale is chosen (nvfp4_quantize_nvfp4 only). */
 typedef enum nvfp4_scale_rule {
   NVFP4_SCALE_MAX6 = 0,    /* block maximum mapped to 6: e = E4M3((a/6)/s_t)   */
-  NVFP4_SCALE_4OVER6 = 1   /* Four Over Six: the better of maximum -> 6 and
+  NVFP4_SCALE_4OVER6 = 1,  /* Four Over Six: the better of maximum -> 6 and
                               maximum -> 4, s_t = max|z| / (6 * 256)           */
+  NVFP4_SCALE_SEARCH = 2   /* the best of the 19 E4M3 scales e0-9 .. e0+9 around
+                              the MAX6 byte e0, s_t = max|z| / (6 * 448)       */
 } nvfp4_scale_rule;
 
 typedef struct nvfp4_opts {
@@ -106,7 +108,7 @@ typedef struct nvfp4_opts {
   int32_t eden_group;      /* MS-EDEN correction group: 128 (default) or 16    */
   const float *tensor_scale_in; /* DEVICE pointer to a given fp32 tensor scale,
                               or NULL to compute it from this tensor           */
-  int32_t scale_rule;      /* nvfp4_scale_rule; NVFP4_SCALE_4OVER6 needs RTN   */
+  int32_t scale_rule;      /* nvfp4_scale_rule; other than MAX6 needs RTN      */
 } nvfp4_opts;
 
 /* Fills *o with defaults: RTN, axis 0, no rotation, seed 0, stream 0,
@@ -143,6 +145,13 @@ size_t nvfp4_workspace_size(int64_t rows, int64_t cols, const nvfp4_opts *o);
  *      e = E4M3((a/6)/s_t) and with e = E4M3((a/4)/s_t), and keeps the one
  *      with the smaller pairwise sum of squared errors (ties keep a/6).
  *      Output is plain NVFP4 (dequantize with NVFP4_FORMAT_NVFP4).
+ *   5. RTN with scale_rule NVFP4_SCALE_SEARCH (a searched block scale [PAL
+ *      "The two corners, and what the palette does to them"; the ScaleSearch
+ *      abstract among the IF4 page's related papers]): s_t as in 2; every
+ *      block is coded by RTN at the scale bytes e0, e0-1, e0+1, ..., e0-9,
+ *      e0+9 (e0 = E4M3((a/6)/s_t); bytes outside 1..126 skipped) and keeps
+ *      the first with a strictly smaller pairwise sum of squared errors.
+ *      Output is plain NVFP4.
  * x: device, in_dtype elements, row-major with leading dimension ld >= cols
  * (elements).  axis 0 needs a 16-byte aligned base and ld * sizeof(elem) a
  * multiple of 16; axis 1 needs only element alignment (16-byte aligned rows

@@ -17,13 +17,13 @@ import numpy as np
 __all__ = [
     "RTN", "SR", "MSEDEN", "FORMAT_NVFP4", "FORMAT_IF4", "QTensor", "NvFp4Error",
     "lib", "signs_to_words", "workspace_size", "quantize_nvfp4", "quantize_if4",
-    "dequantize", "gemm_nvfp4", "rht", "abi_version", "SCALE_MAX6", "SCALE_4OVER6",
+    "dequantize", "gemm_nvfp4", "rht", "abi_version", "SCALE_MAX6", "SCALE_4OVER6", "SCALE_SEARCH",
     "quantize_nvfp4_dual", "workspace_size_dual",
 ]
 
 RTN, SR, MSEDEN = 0, 1, 2
 FORMAT_NVFP4, FORMAT_IF4 = 0, 1
-SCALE_MAX6, SCALE_4OVER6 = 0, 1
+SCALE_MAX6, SCALE_4OVER6, SCALE_SEARCH = 0, 1, 2
 _F32, _BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -132,7 +132,8 @@ def _dtype_code(t, torch):
 
 
 _SCALE_RULE = {"max6": SCALE_MAX6, "4over6": SCALE_4OVER6, "four_over_six": SCALE_4OVER6,
-               SCALE_MAX6: SCALE_MAX6, SCALE_4OVER6: SCALE_4OVER6}
+               "search": SCALE_SEARCH, SCALE_MAX6: SCALE_MAX6, SCALE_4OVER6: SCALE_4OVER6,
+               SCALE_SEARCH: SCALE_SEARCH}
 
 
 def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule=SCALE_MAX6):
@@ -215,7 +216,8 @@ def quantize_nvfp4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0,
     """NVFP4 quantization of a 2-D float32/bfloat16 device tensor (see
     ``nvfp4_quantize_nvfp4`` in include/nvfp4.h).  rht_signs: 128 flags or 4
     words enable the randomized Hadamard rotation.  scale_rule "4over6"
-    selects Four Over Six block scaling (RTN only).  Returns a QTensor."""
+    selects Four Over Six block scaling, "search" a searched block scale
+    (both RTN only).  Returns a QTensor."""
     return _quantize(lib().nvfp4_quantize_nvfp4, x, rounding, axis, rht_signs, seed, stream_id,
                      eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4, scale_rule)
 

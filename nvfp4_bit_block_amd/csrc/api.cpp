@@ -60,10 +60,11 @@ int check_input(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t
     return fail(NVFP4_INVALID_ARG, "IF4 quantization takes rounding RTN only");
   if (o->axis != 0 && o->axis != 1) return fail(NVFP4_INVALID_ARG, "axis %d is not 0 or 1", o->axis);
   if (o->rht != 0 && o->rht != 1) return fail(NVFP4_INVALID_ARG, "rht %d is not 0 or 1", o->rht);
-  if (o->scale_rule != NVFP4_SCALE_MAX6 && o->scale_rule != NVFP4_SCALE_4OVER6)
-    return fail(NVFP4_INVALID_ARG, "scale_rule %d is not MAX6 or 4OVER6", o->scale_rule);
-  if (o->scale_rule == NVFP4_SCALE_4OVER6 && (if4 || o->rounding != NVFP4_RTN))
-    return fail(NVFP4_INVALID_ARG, "Four Over Six scaling takes NVFP4 with rounding RTN only");
+  if (o->scale_rule != NVFP4_SCALE_MAX6 && o->scale_rule != NVFP4_SCALE_4OVER6 &&
+      o->scale_rule != NVFP4_SCALE_SEARCH)
+    return fail(NVFP4_INVALID_ARG, "scale_rule %d is not MAX6, 4OVER6 or SEARCH", o->scale_rule);
+  if (o->scale_rule != NVFP4_SCALE_MAX6 && (if4 || o->rounding != NVFP4_RTN))
+    return fail(NVFP4_INVALID_ARG, "scale rules other than MAX6 take NVFP4 with rounding RTN only");
   if (o->rounding == NVFP4_MSEDEN && o->eden_group != 128 && o->eden_group != 16)
     return fail(NVFP4_INVALID_ARG, "eden_group %d is not 128 or 16", o->eden_group);
   if (rows < 0 || cols < 0)
@@ -191,6 +192,7 @@ int quantize_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, int64
     const Mode m = if4 ? kIf4
                    : o->rounding == NVFP4_SR ? kSr
                    : o->scale_rule == NVFP4_SCALE_4OVER6 ? kFos
+                   : o->scale_rule == NVFP4_SCALE_SEARCH ? kSearch
                                                          : kRtn;
     if (!o->tensor_scale_in) {
       e = launch_quant(p, bf, o->axis, kAmax, grid, s);

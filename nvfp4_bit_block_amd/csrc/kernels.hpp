@@ -17,7 +17,8 @@ enum Mode : int {
   kEden = 4,       // MS-EDEN pass 1: codes + target scales + partial maxima
   kEdenFused = 5,  // MS-EDEN with a given tensor scale: codes + scales in one pass
   kRot = 6,        // rotation only: rotated fp32 values
-  kFos = 7         // NVFP4 RTN, Four Over Six block scale (maximum -> 6 or 4)
+  kFos = 7,        // NVFP4 RTN, Four Over Six block scale (maximum -> 6 or 4)
+  kSearch = 8      // NVFP4 RTN, block scale searched over 19 E4M3 bytes
 };
 
 constexpr int kThreads = 256;      // threads per workgroup of every quantizer

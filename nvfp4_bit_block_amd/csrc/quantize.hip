@@ -189,6 +189,41 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
         store_codes(p, gb, use4 ? lo4 : lo6, use4 ? hi4 : hi6);
         p.scales[gb] = (uint8_t)(use4 ? e4 : e6);
       }
+    } else if constexpr (MODE == kSearch) {
+      // RTN at the scale bytes e0, e0-1, e0+1, ..., e0-9, e0+9 (those in
+      // 1..126; e0 always); keep the first strictly smaller pairwise SSE.
+      const int e0 = (int)e4m3_rne_sat(div_by<6>(a) / s_t);
+      uint32_t best_e = 0, blo = 0, bhi = 0;
+      float best = 0.0f;
+#pragma unroll 1
+      for (int t = 0; t < 19; ++t) {
+        const int e = e0 + (t + 1) / 2 * ((t & 1) ? -1 : 1);
+        if (t > 0 && (e < 1 || e > 126)) continue;
+        const float S = e4m3_value((uint32_t)e) * s_t;
+        const float r = e ? 1.0f / S : 0.0f;
+        float y[16], v[16], sq[16];
+        uint32_t lo, hi;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = z[i] * r;  // r = 0 when e = 0: signed zeros
+        e2m1x16_rne(y, lo, hi);
+        e2m1x16_value(lo, hi, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float d = z[i] - v[i] * S;
+          sq[i] = d * d;
+        }
+        const float sse = tree16(sq);
+        if (t == 0 || sse < best) {
+          best = sse;
+          best_e = (uint32_t)e;
+          blo = lo;
+          bhi = hi;
+        }
+      }
+      if (active) {
+        store_codes(p, gb, blo, bhi);
+        p.scales[gb] = (uint8_t)best_e;
+      }
     } else if constexpr (MODE == kEden || MODE == kEdenFused) {
       // RTN codes under the exact scale a/6; correction c = sum z^2 /
       // sum z*zhat over the group; target t = (a/6) * c.
@@ -276,7 +311,8 @@ template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
-  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kEdenFused) {
+  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kSearch ||
+                MODE == kEdenFused) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
@@ -377,7 +413,8 @@ template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
-  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kEdenFused) {
+  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kSearch ||
+                MODE == kEdenFused) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
@@ -533,6 +570,7 @@ static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid
     case kEdenFused: launch_one<IN_BF16, kEdenFused>(p, axis, grid, s); break;
     case kRot: launch_one<IN_BF16, kRot>(p, axis, grid, s); break;
     case kFos: launch_one<IN_BF16, kFos>(p, axis, grid, s); break;
+    case kSearch: launch_one<IN_BF16, kSearch>(p, axis, grid, s); break;
   }
 }
 

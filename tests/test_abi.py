@@ -99,7 +99,8 @@ def test_quantize_rejections(nv):
     assert _q(nv, ws=FAKE + 16) == MISALIGNED
     assert _q(nv, ws_bytes=100) == WS_SMALL
     assert _q(nv, fn="nvfp4_quantize_if4", rounding=1) == INVALID
-    assert _q(nv, scale_rule=2) == INVALID
+    assert _q(nv, scale_rule=3) == INVALID
+    assert _q(nv, scale_rule=2, rounding=1) == INVALID        # scale search: RTN only
     assert _q(nv, scale_rule=1, rounding=1) == INVALID        # Four Over Six: RTN only
     assert _q(nv, scale_rule=1, rounding=2) == INVALID
     assert _q(nv, fn="nvfp4_quantize_if4", scale_rule=1) == INVALID

@@ -131,6 +131,21 @@ def test_mlp_dy_dual_axis(nv, mlp):
         assert_rotated_close(q_to_host(q), ref, what=f"dY dual axis{axis}")
 
 
+def test_mlp_forward_scale_search(nv, mlp):
+    """The forward operands with a searched block scale, full size, bit-exact;
+    then Y = X W^T on sampled entries."""
+    import torch
+    x, wt, _, _ = mlp
+    gx = nv.quantize_nvfp4(to_device(x, "bf16"), scale_rule="search")
+    gw = nv.quantize_nvfp4(to_device(wt, "bf16"), scale_rule="search")
+    rx = oracle.quantize(x, fmt=oracle.FMT_NVFP4_SEARCH)
+    rw = oracle.quantize(wt, fmt=oracle.FMT_NVFP4_SEARCH)
+    assert_bit_exact(q_to_host(gx), rx, "X search")
+    assert_bit_exact(q_to_host(gw), rw, "W search")
+    c = nv.gemm_nvfp4(gx, gw, out_dtype=torch.float32).cpu().numpy()
+    sampled_gemm_check(nv, rx, rw, c, seed=5)
+
+
 def test_mlp_forward_four_over_six(nv, mlp):
     """The forward pass with Four Over Six scaling of X and W: both operands
     bit-exact at full size, then Y = X W^T on sampled entries."""

@@ -127,6 +127,49 @@ def test_four_over_six_rotation_and_given_scale(nv, axis):
     assert_bit_exact(g, ref, f"4over6 given scale axis{axis}")
 
 
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_scale_search_bit_exact(nv, axis, dtype):
+    """RTN with a searched block scale: codes, scales, tensor scale bit-exact,
+    including rows so small that the standard scale byte underflows to 0."""
+    shapes = ROW_SHAPES if axis == 0 else COL_SHAPES
+    moved = 0
+    for i, (r, c) in enumerate(shapes):
+        x = synth.gradient(r, c, seed=700 + i)[0] if dtype == "bf16" else synth.gaussian(r, c, seed=700 + i)
+        g = q_to_host(nv.quantize_nvfp4(to_device(x, dtype), axis=axis, scale_rule="search"))
+        ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_SEARCH, axis=axis)
+        assert_bit_exact(g, ref, f"search {dtype} axis{axis} {r}x{c}")
+        moved += int(np.sum(ref["scales"] != oracle.quantize(x, axis=axis)["scales"]))
+    assert moved > 0
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((96, 256)).astype(np.float32)
+    x *= (2.0 ** -(np.arange(96) % 31)).astype(np.float32)[:, None]
+    if axis == 1:
+        x = np.ascontiguousarray(x.T)
+    if dtype == "bf16":
+        x = synth.to_bf16_f32(x)
+    g = q_to_host(nv.quantize_nvfp4(to_device(x, dtype), axis=axis, scale_rule="search"))
+    ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_SEARCH, axis=axis)
+    assert_bit_exact(g, ref, f"search tiny rows {dtype} axis{axis}")
+    assert np.any(oracle.quantize(x, axis=axis)["scales"] == 0)
+
+
+def test_scale_search_rotation_and_given_scale(nv):
+    import torch
+    rng = np.random.default_rng(43)
+    signs = synth.signs_from_rng(rng)
+    w = oracle.signs_words(signs)
+    x = synth.gradient(256, 384, seed=710)[0]
+    g = q_to_host(nv.quantize_nvfp4(to_device(x, "bf16"), rht_signs=signs, scale_rule="search"))
+    ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_SEARCH, rht_on=True, signs_w=w)
+    assert_rotated_close(g, ref, what="search rotation")
+    ts = np.float32(0.0117)
+    g = q_to_host(nv.quantize_nvfp4(to_device(x, "bf16"), scale_rule="search",
+                                    tensor_scale_in=torch.tensor([ts], device="cuda:0")))
+    ref = oracle.quantize(x, fmt=oracle.FMT_NVFP4_SEARCH, ts_in=float(ts))
+    assert_bit_exact(g, ref, "search given scale")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("group,rot", [(128, True), (16, True), (128, False), (16, False)])
 def test_dual_axis_mseden(nv, dtype, group, rot):
