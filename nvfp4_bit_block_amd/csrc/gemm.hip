@@ -13,15 +13,16 @@
 // -- and multiplied on the fp16 matrix cores (v_mfma_f32_32x32x16_f16) with
 // fp32 accumulation.
 //
-// Tiling: a workgroup of 4 waves (one per SIMD) computes a 256 x 256 tile;
-// wave (wm, wn) a 128 x 128 sub-tile as 4 x 4 MFMA tiles of 32 x 32 (256 fp32
+// Tiling: a workgroup of 8 waves (two per SIMD, so that one can issue while
+// the other waits on LDS or the barrier) computes a 256 x 256 tile; wave
+// (wm, wn) a 64 x 128 sub-tile as 2 x 4 MFMA tiles of 32 x 32 (128 fp32
 // accumulators per lane).  K advances in chunks of 64 (four 16-wide MFMA
 // steps).  The tile's 16 row fragments per chunk (8 of A, 8 of B, 32 rows
-// each) are split between the waves: each wave loads 4 of them (buffer
-// loads; rows past M or N read as zero), dequantizes them once, and writes
-// the fp16 MFMA operands to LDS in operand order (lane l's 16 bytes at slot
-// l: conflict-free).  Every wave then reads its 4 + 4 operands per step from
-// LDS.  So each fragment is loaded and dequantized once per workgroup, not
+// each) are split between the waves: wave w loads fragment w of A and of B
+// (buffer loads; rows past M or N read as zero), dequantizes them once, and
+// writes the fp16 MFMA operands to LDS in operand order (lane l's 16 bytes at
+// slot l: conflict-free).  Every wave then reads its 2 + 4 operands per step
+// from LDS.  So each fragment is loaded and dequantized once per workgroup, not
 // once per wave that uses it -- the dequantization is the vector-ALU cost
 // that competes with the matrix cores.  LDS is double-buffered (2 x 64 KB):
 // chunk c+1 is dequantized, one step at a time, between the MFMA steps of
@@ -35,7 +36,7 @@
 //
 // Workgroup order: workgroups are dispatched round-robin to the 8 XCDs; the
 // logical tile index is remapped so that each XCD receives a contiguous run,
-// and runs are laid out in groups of 4 tile-rows so that the ~32 workgroups
+// and runs are laid out in groups of 4 tile-rows so that the 32 workgroups
 // resident on one XCD share A and B panels in that XCD's L2.
 #include "kernels.hpp"
 
@@ -46,15 +47,15 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kTile = 256, kWaveTile = 128, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
+constexpr uint32_t kTile = 256, kWaveCols = 128, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;
 
 // Raw codes of this wave's 4 fragments for one chunk: the lane's 32 codes and
 // the chunk's four E4M3 scale bytes of its row -- bytes 2h, 2h+1 are the lane
 // half's (own fragments 0,1 = A, 2,3 = B).
 struct Raw {
-  u32x4_t code[4];
-  uint32_t scale[4];
+  u32x4_t code[2];
+  uint32_t scale[2];
 };
 
 struct Panels {
@@ -63,19 +64,19 @@ struct Panels {
   // and of B) and of its lane half's first k.  The whole row offset is in the
   // vector offset, so rows past M or N fall outside the buffer's range and
   // read as zero; the chunk's k offset (< one row) is the scalar offset.
-  uint32_t vo_c[2], vo_s[2];
+  uint32_t vo_c, vo_s;
   uint32_t K, h;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_c(const Panels &p, int o) { return o < 2 ? p.ac : p.bc; }
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_s(const Panels &p, int o) { return o < 2 ? p.as : p.bs; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_c(const Panels &p, int o) { return o < 1 ? p.ac : p.bc; }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_s(const Panels &p, int o) { return o < 1 ? p.as : p.bs; }
 
 // Whole chunk at k0 < K, K % 64 == 0.
 __device__ __forceinline__ void load_fast(Raw &r, const Panels &p, uint32_t k0) {
 #pragma unroll
-  for (int o = 0; o < 4; ++o) {
-    r.code[o] = __builtin_amdgcn_raw_buffer_load_b128(own_rsrc_c(p, o), p.vo_c[o & 1], k0 / 2, 0);
-    r.scale[o] = __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_s(p, o), p.vo_s[o & 1], k0 / 16, 0);
+  for (int o = 0; o < 2; ++o) {
+    r.code[o] = __builtin_amdgcn_raw_buffer_load_b128(own_rsrc_c(p, o), p.vo_c, k0 / 2, 0);
+    r.scale[o] = __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_s(p, o), p.vo_s, k0 / 16, 0);
   }
 }
 
@@ -83,19 +84,19 @@ __device__ __forceinline__ void load_fast(Raw &r, const Panels &p, uint32_t k0) 
 __device__ __forceinline__ void load_generic(Raw &r, const Panels &p, uint32_t k0) {
   const uint32_t kl = k0 + 32 * p.h;  // first k of this lane's 32
 #pragma unroll
-  for (int o = 0; o < 4; ++o) {
+  for (int o = 0; o < 2; ++o) {
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       w[q] = (kl + 8 * q + 8 <= p.K)
-                 ? __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_c(p, o), p.vo_c[o & 1] + 4 * q, k0 / 2, 0)
+                 ? __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_c(p, o), p.vo_c + 4 * q, k0 / 2, 0)
                  : 0u;
     r.code[o] = u32x4_t{w[0], w[1], w[2], w[3]};
     uint32_t s = 0;
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (kl + 16 * q < p.K)
-        s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(own_rsrc_s(p, o), p.vo_s[o & 1] + 2 * p.h + q,
+        s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(own_rsrc_s(p, o), p.vo_s + 2 * p.h + q,
                                                             k0 / 16, 0)
              << (8 * (q + 2 * p.h));
     r.scale[o] = s;
@@ -151,14 +152,14 @@ typedef half8_t Stage[2][16][kSteps][64];
 // and, for IF4 operands, their INT flags (bits 7 and 15 of f).
 template <int IF4>
 struct Scales {
-  half2_t s[4];
-  uint32_t f[4];
+  half2_t s[2];
+  uint32_t f[2];
 };
 
 template <int IF4>
 __device__ __forceinline__ void scales16(const Raw &r, uint32_t h, Scales<IF4> &sc) {
 #pragma unroll
-  for (int o = 0; o < 4; ++o) {
+  for (int o = 0; o < 2; ++o) {
     const uint32_t b = r.scale[o] >> (16 * h);
     if (IF4) {
       sc.f[o] = b;
@@ -169,12 +170,12 @@ __device__ __forceinline__ void scales16(const Raw &r, uint32_t h, Scales<IF4> &
   }
 }
 
-// Dequantize item q = 4 * step + own fragment (0..15) of a chunk into buffer b.
+// Dequantize item q = 2 * step + own fragment (0..7) of a chunk into buffer b.
 template <int IF4>
 __device__ __forceinline__ void dequant_item(Stage &st, int b, const Raw &r, const Scales<IF4> &sc, uint32_t w,
                                              uint32_t lane, int q) {
-  const int j = q >> 2, o = q & 3;
-  const int frag = o < 2 ? (int)(2 * w) + o : 8 + (int)(2 * w) + (o - 2);
+  const int j = q >> 1, o = q & 1;
+  const int frag = o == 0 ? (int)w : 8 + (int)w;
   if (IF4) {
     const bool is_int = (sc.f[o] >> (8 * (j >> 1) + 7)) & 1u;
     st[b][frag][j][lane] = dequant8_lut(r.code[o][j], sc.s[o][j >> 1], is_int ? kLutIntLo : kLutFpLo,
@@ -185,7 +186,7 @@ __device__ __forceinline__ void dequant_item(Stage &st, int b, const Raw &r, con
 }
 
 struct Ops {
-  half8_t a[4], b[4];
+  half8_t a[2], b[4];
 };
 
 __device__ __forceinline__ void read_ops(Ops &op, const Stage &st, int b, uint32_t wm, uint32_t wn, uint32_t lane,
@@ -193,12 +194,12 @@ __device__ __forceinline__ void read_ops(Ops &op, const Stage &st, int b, uint32
 #pragma unroll
   for (int n = 0; n < 4; ++n) op.b[n] = st[b][8 + 4 * wn + n][j][lane];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) op.a[m] = st[b][4 * wm + m][j][lane];
+  for (int m = 0; m < 2; ++m) op.a[m] = st[b][2 * wm + m][j][lane];
 }
 
-__device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[4][4]) {
+__device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[2][4]) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n)
       acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op.a[m], op.b[n], acc[m][n], 0, 0, 0);
@@ -209,7 +210,7 @@ __device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[4][4]) {
 template <int NV>
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
     __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);   // LDS
@@ -225,7 +226,7 @@ __device__ __forceinline__ void interleave_step() {
 template <int IF4>
 __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Raw &rd, Ops &op, const Panels &p,
                                       uint32_t w, uint32_t wm, uint32_t wn, uint32_t lane,
-                                      float16_t (&acc)[4][4]) {
+                                      float16_t (&acc)[2][4]) {
   const int cur = c & 1, nxt = cur ^ 1;
   Scales<IF4> s;
   scales16<IF4>(rd, p.h, s);
@@ -233,23 +234,23 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
   // step 0
   read_ops(nx, st, cur, wm, wn, lane, 1);
 #pragma unroll
-  for (int q = 0; q < 6; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
+  for (int q = 0; q < 3; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
   mfma16(op, acc);
-  interleave_step<IF4 ? 10 : 3>();
+  interleave_step<IF4 ? 10 : 8>();
   __builtin_amdgcn_sched_barrier(0);
   // step 1
   read_ops(op, st, cur, wm, wn, lane, 2);
 #pragma unroll
-  for (int q = 6; q < 11; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
+  for (int q = 3; q < 6; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
   mfma16(nx, acc);
-  interleave_step<IF4 ? 10 : 3>();
+  interleave_step<IF4 ? 10 : 8>();
   __builtin_amdgcn_sched_barrier(0);
   // step 2
   read_ops(nx, st, cur, wm, wn, lane, 3);
 #pragma unroll
-  for (int q = 11; q < 16; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
+  for (int q = 6; q < 8; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
   mfma16(op, acc);
-  interleave_step<IF4 ? 10 : 3>();
+  interleave_step<IF4 ? 10 : 8>();
   __builtin_amdgcn_sched_barrier(0);
   load_fast(rd, p, k_next);
   __syncthreads();
@@ -261,7 +262,7 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
 }
 
 template <int OUT_BF16, int FAST, int IF4>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(512, 1) void k_gemm(GemmParams p) {
   __shared__ Stage st;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & 63u;
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
   const uint32_t K = p.K, K2 = K / 2, K16 = K / 16;
   const uint32_t m0 = tm * kTile, n0 = tn * kTile;
   const uint32_t rows_a = min(kTile, p.M - m0), rows_b = min(kTile, p.N - n0);
-  const uint32_t wm = w >> 1, wn = w & 1u;
+  const uint32_t wm = w >> 1, wn = w & 1u;   // wave tile: rows 64 wm.., columns 128 wn..
 
   Panels P;
   P.ac = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_codes + (size_t)m0 * K2), (short)0,
@@ -293,18 +294,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
                                            (int)(rows_b * K2), kRsrcWord3);
   P.bs = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_scales + (size_t)n0 * K16), (short)0,
                                            (int)(rows_b * K16), kRsrcWord3);
-#pragma unroll
-  for (int o = 0; o < 2; ++o) {
-    const uint32_t row = 32 * (2 * w + o) + r32;  // this lane's row of own fragment o (A) and o+2 (B)
-    P.vo_c[o] = row * K2 + 16 * h;
-    P.vo_s[o] = row * K16;
+  {
+    const uint32_t row = 32 * w + r32;  // this lane's row of own fragments (A and B)
+    P.vo_c = row * K2 + 16 * h;
+    P.vo_s = row * K16;
   }
   P.K = K;
   P.h = h;
 
-  float16_t acc[4][4];
+  float16_t acc[2][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
       Scales<IF4> s;
       scales16<IF4>(r0, P.h, s);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) dequant_item<IF4>(st, 0, r0, s, w, lane, q);
+      for (int q = 0; q < 8; ++q) dequant_item<IF4>(st, 0, r0, s, w, lane, q);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_fast(r0, P, min(2 * kChunk, klast));
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
     Scales<IF4> s;
     scales16<IF4>(r, P.h, s);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) dequant_item<IF4>(st, 0, r, s, w, lane, q);
+    for (int q = 0; q < 8; ++q) dequant_item<IF4>(st, 0, r, s, w, lane, q);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < (int)kSteps; ++j) {
@@ -366,14 +366,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams p) {
   // and rows 8*(e/4) + 4*h + (e%4), e = 0..15.
   const float alpha = (*p.a_ts) * (*p.b_ts);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < 2; ++m) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const uint32_t col = n0 + wn * kWaveTile + 32 * n + r32;
+      const uint32_t col = n0 + wn * kWaveCols + 32 * n + r32;
       if (col >= p.N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const uint32_t row = m0 + wm * kWaveTile + 32 * m + 8 * (e >> 2) + 4 * h + (e & 3);
+        const uint32_t row = m0 + wm * 64 + 32 * m + 8 * (e >> 2) + 4 * h + (e & 3);
         if (row >= p.M) continue;
         const float v = acc[m][n][e] * alpha;
         if (OUT_BF16) {
@@ -392,11 +392,11 @@ template <int IF4>
 static void launch_fmt(const GemmParams &p, int out_bf16, uint32_t tiles, hipStream_t s) {
   const bool fast = (p.K % 64) == 0;
   if (out_bf16) {
-    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(tiles), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(tiles), dim3(256), 0, s, p);
+    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(tiles), dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(tiles), dim3(512), 0, s, p);
   } else {
-    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(tiles), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(tiles), dim3(256), 0, s, p);
+    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(tiles), dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(tiles), dim3(512), 0, s, p);
   }
 }
 
