@@ -123,6 +123,7 @@ def write_traffic(fetch_dir, write_dir, cal_gib):
     f_scale = cal_bytes / (fetch[cal[0]][0] * 1024.0)
     w_scale = cal_bytes / (write[cal[0]][0] * 1024.0)
     digests = {"k_gemm": source_digest("gemm.hip", "common.hpp", "kernels.hpp"),
+               "k_gemm_if4": source_digest("gemm.hip", "common.hpp", "kernels.hpp"),
                "k_quant": source_digest("quantize.hip", "common.hpp", "kernels.hpp"),
                "k_eden_scales": source_digest("quantize.hip", "common.hpp", "kernels.hpp")}
     out = {"calibration": {"bytes": cal_bytes, "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
@@ -134,7 +135,11 @@ def write_traffic(fetch_dir, write_dir, cal_gib):
         fam = next((d for d in digests if short.startswith(d)), None)
         fb = [v * 1024.0 * f_scale for v in fetch[name]]
         wb = [v * 1024.0 * w_scale for v in write.get(name, [0.0])]
-        fam_key = "k_gemm" if short.startswith("k_gemm") else short
+        if short.startswith("k_gemm"):
+            # k_gemm<OUT_BF16, FAST, IF4>: the step's GEMMs are the NVFP4 ones
+            fam_key = "k_gemm_if4" if short.replace(" ", "").endswith(",1>") else "k_gemm"
+        else:
+            fam_key = short
         e = out.setdefault(fam_key, {"source_digest": digests.get(fam), "instances": {}})
         e["instances"][short] = {"launches": len(fb), "fetch_bytes": [round(x) for x in fb],
                                  "write_bytes": [round(x) for x in wb]}
