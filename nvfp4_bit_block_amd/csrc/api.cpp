@@ -128,8 +128,8 @@ void fill_common(QuantParams &p, const void *x, int in_dtype, int64_t rows, int6
   p.K16 = sh.K / 16;
   p.nblocks = (uint32_t)sh.nblocks;
   p.k16div = make_fastdiv(p.K16 ? p.K16 : 1);
-  // axis 1 tiles: 128 rows x 128 bytes of columns (one tile per wave)
-  const uint32_t tc = in_dtype == NVFP4_BF16 ? 64 : 32;
+  // axis 1 tiles: 128 rows x 8 * kColWords words of columns (one tile per wave)
+  const uint32_t tc = 8u * (in_dtype == NVFP4_BF16 ? 2u * kColWords : (uint32_t)kColWords);
   const uint32_t nct = (uint32_t)((cols + tc - 1) / tc);
   const uint32_t ntt = (uint32_t)((rows + 127) / 128);
   p.ctiles_div = make_fastdiv(nct ? nct : 1);

@@ -23,6 +23,10 @@ enum Mode : int {
 
 constexpr int kThreads = 256;      // threads per workgroup of every quantizer
 constexpr int kMaxPartials = 2048; // workgroups of a pass that writes partials
+// Axis-1 kernels: each lane loads kColWords 32-bit words of each of its 16
+// rows (bf16: 2 columns per word, fp32: 1), so a wave tile is 128 rows x
+// 8 * kColWords words of columns.
+constexpr int kColWords = 4;
 constexpr size_t kPartialBytes = 16384;
 
 struct QuantParams {

@@ -358,21 +358,28 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
 template <int IN_BF16, int MODE>
 __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint32_t tc, uint32_t lig, uint32_t q,
                                          uint32_t sbits, float s_t, float &lmax) {
-  constexpr int CPL = IN_BF16 ? 8 : 4;  // columns per 16-byte chunk
-  constexpr int TCOL = 8 * CPL;         // columns per wave tile
+  constexpr int CPL = IN_BF16 ? 2 * kColWords : kColWords;  // columns per lane
+  constexpr int TCOL = 8 * CPL;                              // columns per wave tile
   const uint32_t row0 = tt * 128 + 16 * lig;     // this lane's 16 rows
   const uint32_t col0 = tc * TCOL + CPL * q;     // this lane's CPL columns
   const bool rows_ok = row0 < p.rows;            // rows % 16 == 0: whole slab or nothing
-  uint32_t w[16][4];
+  uint32_t w[16][kColWords];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0u;
+#pragma unroll
+    for (int c = 0; c < kColWords; ++c) w[r][c] = 0u;
     if (rows_ok && col0 < p.cols) {
       const size_t off = (size_t)(row0 + r) * p.ld + col0;
+      const void *src = IN_BF16 ? static_cast<const void *>(static_cast<const uint16_t *>(p.x) + off)
+                                : static_cast<const void *>(static_cast<const float *>(p.x) + off);
       if (p.vec && col0 + CPL <= p.cols) {
-        const uint4 a = IN_BF16 ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + off)
-                                : *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.x) + off);
-        w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+        if constexpr (kColWords == 4) {
+          const uint4 a = *static_cast<const uint4 *>(src);
+          w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
+        } else {
+          const uint2 a = *static_cast<const uint2 *>(src);
+          w[r][0] = a.x; w[r][1] = a.y;
+        }
       } else if (IN_BF16) {  // (fully unrolled: a runtime index would put w in scratch)
         const uint16_t *src = static_cast<const uint16_t *>(p.x) + off;
 #pragma unroll
@@ -387,7 +394,7 @@ __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint
     }
     const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w[r][c] ^= sflip;
+    for (int c = 0; c < kColWords; ++c) w[r][c] ^= sflip;
   }
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
 // its own partial maxima and target scales.
 template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantParams pc) {
-  constexpr int CPL = IN_BF16 ? 8 : 4;
+  constexpr int CPL = IN_BF16 ? 2 * kColWords : kColWords;
   constexpr int TCOL = 8 * CPL;
   constexpr uint32_t kWidth = 4 * TCOL;      // tile columns
   constexpr uint32_t kBpr = kWidth / 16;     // row blocks per tile row
@@ -584,7 +591,7 @@ hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, 
 }
 
 uint32_t dual_grid(const QuantParams &pr, int in_bf16) {
-  const uint32_t width = in_bf16 ? 256u : 128u;
+  const uint32_t width = 4u * 8u * (in_bf16 ? 2u * kColWords : (uint32_t)kColWords);
   const uint64_t tiles = (uint64_t)(pr.rows / 128) * ((pr.cols + width - 1) / width);
   uint64_t g = tiles < 1 ? 1 : tiles;
   return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);
