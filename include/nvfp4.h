@@ -176,7 +176,8 @@ int nvfp4_quantize_nvfp4(const void *x, int in_dtype, int64_t rows, int64_t cols
  * scales_c, ts_c: [cols x rows/2], [cols x rows/16]); o->axis is ignored,
  * o->rounding must be NVFP4_MSEDEN, and each output has its own tensor scale
  * (both equal *o->tensor_scale_in when it is given).  Both axes must meet the
- * shape rules (multiples of 16, of 128 with rotation or group 128) and x the
+ * shape rules (multiples of 16, of 128 with rotation or group 128), rows must
+ * be a multiple of 128 in any case (NVFP4_BAD_SHAPE), and x must meet the
  * axis-0 alignment.  ws: at least nvfp4_workspace_size_dual() bytes,
  * 256-byte aligned.
  */

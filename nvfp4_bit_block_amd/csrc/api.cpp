@@ -218,6 +218,9 @@ int quantize_dual_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, 
   int st = check_input(x, in_dtype, rows, cols, ld, &orow, false, &shr);
   if (!st) st = check_input(x, in_dtype, rows, cols, ld, &ocol, false, &shc);
   if (st) return st;
+  if (rows % 128)  // the kernel works on tiles of 128 whole rows
+    return fail(NVFP4_BAD_SHAPE, "the two-axis quantization needs rows %% 128 == 0 (rows = %lld)",
+                (long long)rows);
   const size_t wr = nvfp4_workspace_size(rows, cols, &orow);
   if (ws_bytes < wr) return fail(NVFP4_WS_TOO_SMALL, "workspace of %zu bytes is below the %zu required",
                                  ws_bytes, nvfp4_workspace_size_dual(rows, cols, o));

@@ -124,6 +124,7 @@ def test_dual_rejections_and_workspace(nv):
     assert d(rows=100) == SHAPE                      # the column-wise K = rows
     assert d(cols=200) == SHAPE
     assert d(rows=144) == SHAPE                      # group 128 along the rows
+    assert d(rows=144, eden_group=16) == SHAPE       # group 16: still whole 128-row tiles
     assert d(ws_bytes=w0) == WS_SMALL
 
 
