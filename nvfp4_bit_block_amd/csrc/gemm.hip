@@ -50,9 +50,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr uint32_t kTile = 256, kWaveCols = 128, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
 constexpr int kRsrcWord3 = 0x00020000;
 
-// Raw codes of this wave's 4 fragments for one chunk: the lane's 32 codes and
-// the chunk's four E4M3 scale bytes of its row -- bytes 2h, 2h+1 are the lane
-// half's (own fragments 0,1 = A, 2,3 = B).
+// Raw codes of this wave's 2 fragments for one chunk (own fragment 0 = A,
+// 1 = B): the lane's 32 codes and the chunk's four E4M3 scale bytes of its
+// row -- bytes 2h, 2h+1 are the lane half's.
 struct Raw {
   u32x4_t code[2];
   uint32_t scale[2];
@@ -60,10 +60,11 @@ struct Raw {
 
 struct Panels {
   __amdgpu_buffer_rsrc_t ac, as, bc, bs;  // codes / scales of this tile's rows
-  // Byte offset of this lane's row of own fragment 0 / 1 (the same rows of A
-  // and of B) and of its lane half's first k.  The whole row offset is in the
-  // vector offset, so rows past M or N fall outside the buffer's range and
-  // read as zero; the chunk's k offset (< one row) is the scalar offset.
+  // vo_c: byte offset of this lane's row of its own fragments (the same row
+  // index in A and in B) plus its lane half's first code byte; vo_s: that
+  // row's first scale byte.  The whole row offset is in the vector offset, so
+  // rows past M or N fall outside the buffer's range and read as zero; the
+  // chunk's k offset (< one row) is the scalar offset.
   uint32_t vo_c, vo_s;
   uint32_t K, h;
 };
