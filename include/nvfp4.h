@@ -155,7 +155,8 @@ size_t nvfp4_workspace_size(int64_t rows, int64_t cols, const nvfp4_opts *o);
  * x: device, in_dtype elements, row-major with leading dimension ld >= cols
  * (elements).  axis 0 needs a 16-byte aligned base and ld * sizeof(elem) a
  * multiple of 16; axis 1 needs only element alignment (16-byte aligned rows
- * are loaded with vector loads, others element by element).
+ * are loaded with vector loads, others element by element) and a row stride
+ * ld * sizeof(elem) of at most 16 MiB (else NVFP4_UNSUPPORTED).
  * codes / scales: device, 16-byte aligned, sizes as in the layout above.
  * tensor_scale: device fp32 written with s_t (copied from tensor_scale_in if
  * given).  ws: device workspace of at least nvfp4_workspace_size() bytes,
@@ -178,7 +179,7 @@ int nvfp4_quantize_nvfp4(const void *x, int in_dtype, int64_t rows, int64_t cols
  * (both equal *o->tensor_scale_in when it is given).  Both axes must meet the
  * shape rules (multiples of 16, of 128 with rotation or group 128), rows must
  * be a multiple of 128 in any case (NVFP4_BAD_SHAPE), and x must meet the
- * axis-0 alignment.  ws: at least nvfp4_workspace_size_dual() bytes,
+ * axis-0 alignment and the axis-1 stride limit.  ws: at least nvfp4_workspace_size_dual() bytes,
  * 256-byte aligned.
  */
 int nvfp4_quantize_nvfp4_dual(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,

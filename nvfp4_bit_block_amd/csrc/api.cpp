@@ -40,6 +40,7 @@ size_t elem_size(int dtype) { return dtype == NVFP4_BF16 ? 2 : 4; }
 // Blocks (of 16 output elements) a quantizer writes; limits of this build.
 constexpr uint64_t kMaxBlocks = (1ull << 31) - 1;
 constexpr uint64_t kMaxDim = (1ull << 31) - 1;
+constexpr uint64_t kMaxColStride = 1ull << 24;  // bytes per input row, axis 1
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -72,6 +73,10 @@ int check_input(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t
   if ((uint64_t)rows > kMaxDim || (uint64_t)cols > kMaxDim)
     return fail(NVFP4_UNSUPPORTED, "dimension above 2^31 - 1");
   if (ld < cols) return fail(NVFP4_BAD_SHAPE, "ld %lld < cols %lld", (long long)ld, (long long)cols);
+  // the column-wise kernels address a 128-row tile with 32-bit offsets
+  if (o->axis == 1 && (uint64_t)ld * elem_size(in_dtype) > kMaxColStride)
+    return fail(NVFP4_UNSUPPORTED, "axis 1: a row stride of %llu bytes is above 16 MiB",
+                (unsigned long long)((uint64_t)ld * elem_size(in_dtype)));
   const int64_t R = o->axis == 0 ? rows : cols;
   const int64_t K = o->axis == 0 ? cols : rows;
   if (K % 16)

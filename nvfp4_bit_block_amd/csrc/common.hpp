@@ -17,6 +17,9 @@ namespace nv4 {
 
 constexpr int kWave = 64;
 
+// Word 3 of a raw (unswizzled, offset-addressed) buffer resource on gfx950.
+constexpr int kRsrcWord3 = 0x00020000;
+
 // ---------------------------------------------------------------- bits
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -310,6 +313,78 @@ __device__ __forceinline__ void fwht128_group(float v[16], uint32_t pos) {
   const float c = 0x1.6a09e6p-4f;  // fp32(1/sqrt(128)) = 0x3DB504F3
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = v[i] * c;
+}
+
+// The same rotation with one instruction per cross-lane stage instead of two.
+// Every lane computes own + k * partner, which a DPP-sourced fused
+// multiply-add does in one step: the lower lane gets a + b, the upper lane
+// b - a, the negation of its a - b.  Rounding to nearest is symmetric, so the
+// upper lane's value is exactly the negated result, up to the sign of an
+// exact zero (x - x is +0 either way round).  Partners in the later stages
+// share their negation, so k stays +1 / -1; after the three stages a lane's
+// values carry the sign (-1)^popcount(pos), folded into the normalization.
+// Nonzero outputs are bit-identical to fwht128_group.  A zero output may
+// carry the other sign, so the function returns true -- in every lane of the
+// wave -- when some lane of the wave holds a zero; the caller then
+// recomputes with fwht128_group.
+//
+// The compiler does not fuse a DPP move into v_fmac_f32, so the stage is
+// written out: v_fmac_f32_dpp d, d, k computes d + k * (d of the partner
+// lane) -- every lane reads its partner's d before any lane writes.  The
+// leading s_nop 4 gives the wait states that a DPP read needs after a vector
+// write of its source register (2) or of EXEC (5); inside the block no
+// instruction reads a register that an earlier one wrote.
+#define NV4_FMAC_DPP16(CTRL)                                                                      \
+  "s_nop 4\n\t"                                                                                   \
+  "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
+  "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                         \
+  "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                         \
+  "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                         \
+  "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                         \
+  "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                         \
+  "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf"
+
+#define NV4_V16(v)                                                                                 \
+  "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),  \
+      "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),     \
+      "+v"(v[15])
+
+template <int S>
+__device__ __forceinline__ void fwht_cross_negating(float v[16], float k) {
+  if constexpr (S == 1) {
+    asm volatile(NV4_FMAC_DPP16("quad_perm:[1,0,3,2]") : NV4_V16(v) : "v"(k));
+  } else if constexpr (S == 2) {
+    asm volatile(NV4_FMAC_DPP16("quad_perm:[2,3,0,1]") : NV4_V16(v) : "v"(k));
+  } else {
+    static_assert(S == 4, "fwht_cross_negating supports group bits 1, 2, 4");
+    asm volatile(NV4_FMAC_DPP16("row_ror:8") : NV4_V16(v) : "v"(k));
+  }
+}
+#undef NV4_FMAC_DPP16
+#undef NV4_V16
+
+__device__ __forceinline__ bool fwht128_group_fast(float v[16], uint32_t pos) {
+  fwht16_inlane(v);
+  fwht_cross_negating<1>(v, (pos & 1u) ? -1.0f : 1.0f);
+  fwht_cross_negating<2>(v, (pos & 2u) ? -1.0f : 1.0f);
+  fwht_cross_negating<4>(v, (pos & 4u) ? -1.0f : 1.0f);
+  const float c = (__builtin_popcount(pos) & 1) ? -0x1.6a09e6p-4f : 0x1.6a09e6p-4f;
+  float m = __builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = v[i] * c;
+    m = fminf(m, fabsf(v[i]));
+  }
+  return __builtin_amdgcn_ballot_w64(m == 0.0f) != 0;
 }
 
 // 16 sign bits of a lane's coordinate block within the 128-bit sign vector.

@@ -48,7 +48,6 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kTile = 256, kWaveCols = 128, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
-constexpr int kRsrcWord3 = 0x00020000;
 
 // Raw codes of this wave's 2 fragments for one chunk (own fragment 0 = A,
 // 1 = B): the lane's 32 codes and the chunk's four E4M3 scale bytes of its

@@ -307,6 +307,24 @@ __device__ __forceinline__ void unpack_block(const RawBlock<IN_BF16> &b, const S
   else unpack_f32(w, sm, z);
 }
 
+// Unpack and rotate one lane's block: the one-instruction cross-lane stages,
+// redone with the exact two-instruction ones when the wave holds a zero
+// output (whose sign the fast stages may get wrong).
+template <int IN_BF16>
+__device__ __forceinline__ void load_z(const RawBlock<IN_BF16> &b, const SignMasks &sm, bool rht, uint32_t lig,
+                                       float z[16]) {
+  unpack_block<IN_BF16>(b, sm, z);
+  if (rht && fwht128_group_fast(z, lig)) {
+    // (the raw words pass through an empty asm so that the compiler cannot
+    // keep the in-lane stages' results alive from the fast path for reuse)
+    RawBlock<IN_BF16> c = b;
+#pragma unroll
+    for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) asm volatile("" : "+v"(c.q[i].x), "+v"(c.q[i].y), "+v"(c.q[i].z), "+v"(c.q[i].w));
+    unpack_block<IN_BF16>(c, sm, z);
+    fwht128_group(z, lig);
+  }
+}
+
 template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   __shared__ float red[kThreads / kWave];
@@ -333,8 +351,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
     // lanes past the end hold stale values; they fill whole rotation groups
     // and store nothing, so they never reach an output
     float z[16];
-    unpack_block<IN_BF16>(cur, sm, z);
-    if (p.rht) fwht128_group(z, lig);
+    load_z<IN_BF16>(cur, sm, p.rht, lig, z);
     quant_block<MODE>(z, gb, active, p, s_t, lmax);
     cur = nxt;
   }
@@ -346,71 +363,111 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
 
 // ---------------------------------------------------------------- axis 1
 // A wave's tile is 128 positions along the reduction (input rows) x 128 bytes
-// of columns.  Lane (q = lane / 8, lig = lane % 8) loads the 16 rows
-// T0 + 16 lig .. + 15 of the 16-byte column chunk q: it then holds the
-// 16-element blocks of that chunk's 8 (bf16) or 4 (fp32) columns, and the 8
-// lanes with the same q hold one 128-position rotation group per column.
-// Each load instruction reads 8 rows x 128 contiguous bytes; no LDS is used.
-// The rotation sign of a position is the same for every column, so it is
-// XORed into each raw row word once.
-// One wave's column tile (tile row tt, tile column tc): 128 positions along
-// the reduction x TCOL columns; see k_quant_cols.
+// of columns (64 bf16 or 32 fp32 columns).  Lane (q = lane bits 2, 4, 5;
+// lig = group position) holds the rows T0 + 16 lig .. + 15 of the 16-byte
+// column chunk q: the 16-element blocks of that chunk's kColCols columns, and
+// the 8 lanes with the same q hold one 128-position rotation group per
+// column.  Each load instruction reads 8 rows x 128 contiguous bytes (a
+// buffer load whose row offset is a scalar); no LDS is used.  The rotation
+// sign of a position is the same for every column: one mask per row.
+template <int IN_BF16>
+struct ColCfg {
+  static constexpr uint32_t kEs = IN_BF16 ? 2 : 4;                        // input element bytes
+  static constexpr uint32_t kColCols = IN_BF16 ? 2 * kColWords : kColWords; // columns per lane
+  static constexpr uint32_t kTileCols = 8 * kColCols;                      // columns per wave tile
+};
+static_assert(kColWords == 4, "a lane loads one 16-byte chunk per row");
+
+// Raw words of a lane's 16 rows x 16 bytes.
+typedef uint32_t ColRaw[16][kColWords];
+
+// Load tile (tt, tc) for this lane (zeros outside the tensor).  The buffer
+// starts at the tile's first row: offsets within a 128-row tile stay below
+// 2^31 for rows of up to 16 MiB.
+template <int IN_BF16>
+__device__ __forceinline__ void col_load(const QuantParams &p, uint32_t tt, uint32_t tc, uint32_t lig, uint32_t q,
+                                         ColRaw &w) {
+  using C = ColCfg<IN_BF16>;
+  const uint32_t row0 = tt * 128 + 16 * lig;
+  const uint32_t c0 = tc * C::kTileCols + C::kColCols * q;
+  const uint64_t tile_off = (uint64_t)(tt * 128) * (uint64_t)p.ld * C::kEs;
+  const uint64_t end = ((uint64_t)(p.rows - 1) * (uint64_t)p.ld + p.cols) * C::kEs;
+  const uint64_t left = end > tile_off ? end - tile_off : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(static_cast<const uint8_t *>(p.x) + tile_off), (short)0,
+      (int)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull), kRsrcWord3);
+  const uint32_t step = (uint32_t)p.ld * C::kEs;  // bytes per input row
+  const uint32_t vo = (16 * lig * (uint32_t)p.ld + c0) * C::kEs;
+  const bool any = row0 < p.rows && c0 < p.cols;  // rows % 16 == 0: whole slab or nothing
+  const bool full = any && p.vec && c0 + C::kColCols <= p.cols;
+  // (one choice for the whole wave: were lanes to differ, the zeroing below
+  // would have to wait for the other lanes' loads into the same registers)
+  if (__builtin_amdgcn_ballot_w64(!full) == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, r * step, 0);
+#pragma unroll
+      for (int c = 0; c < kColWords; ++c) w[r][c] = v[c];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int c = 0; c < kColWords; ++c) w[r][c] = 0u;
+    if (any) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (uint32_t j = 0; j < C::kColCols; ++j) {
+          if (c0 + j >= p.cols) continue;
+          if (IN_BF16)
+            w[r][j >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, vo + 2 * j, r * step, 0)
+                            << (16 * (j & 1));
+          else
+            w[r][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4 * j, r * step, 0);
+        }
+      }
+    }
+  }
+}
+
+// One wave tile (tile row tt, tile column tc).
 template <int IN_BF16, int MODE>
 __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint32_t tc, uint32_t lig, uint32_t q,
                                          uint32_t sbits, float s_t, float &lmax) {
-  constexpr int CPL = IN_BF16 ? 2 * kColWords : kColWords;  // columns per lane
-  constexpr int TCOL = 8 * CPL;                              // columns per wave tile
-  const uint32_t row0 = tt * 128 + 16 * lig;     // this lane's 16 rows
-  const uint32_t col0 = tc * TCOL + CPL * q;     // this lane's CPL columns
-  const bool rows_ok = row0 < p.rows;            // rows % 16 == 0: whole slab or nothing
-  uint32_t w[16][kColWords];
+  using C = ColCfg<IN_BF16>;
+  ColRaw w;
+  col_load<IN_BF16>(p, tt, tc, lig, q, w);
+  const uint32_t row0 = tt * 128 + 16 * lig;
+  const uint32_t c0 = tc * C::kTileCols + C::kColCols * q;
+  const bool rows_ok = row0 < p.rows;
+  const uint32_t kblk = tt * 8 + lig;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (uint32_t j = 0; j < C::kColCols; ++j) {
+    const int wi = IN_BF16 ? (int)(j >> 1) : (int)j;
+    uint32_t cw[16];
 #pragma unroll
-    for (int c = 0; c < kColWords; ++c) w[r][c] = 0u;
-    if (rows_ok && col0 < p.cols) {
-      const size_t off = (size_t)(row0 + r) * p.ld + col0;
-      const void *src = IN_BF16 ? static_cast<const void *>(static_cast<const uint16_t *>(p.x) + off)
-                                : static_cast<const void *>(static_cast<const float *>(p.x) + off);
-      if (p.vec && col0 + CPL <= p.cols) {
-        if constexpr (kColWords == 4) {
-          const uint4 a = *static_cast<const uint4 *>(src);
-          w[r][0] = a.x; w[r][1] = a.y; w[r][2] = a.z; w[r][3] = a.w;
-        } else {
-          const uint2 a = *static_cast<const uint2 *>(src);
-          w[r][0] = a.x; w[r][1] = a.y;
-        }
-      } else if (IN_BF16) {  // (fully unrolled: a runtime index would put w in scratch)
-        const uint16_t *src = static_cast<const uint16_t *>(p.x) + off;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          if (col0 + j < p.cols) w[r][j >> 1] |= (uint32_t)src[j] << (16 * (j & 1));
-      } else {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(static_cast<const float *>(p.x) + off);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          if (col0 + j < p.cols) w[r][j] = src[j];
-      }
-    }
-    const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
-#pragma unroll
-    for (int c = 0; c < kColWords; ++c) w[r][c] ^= sflip;
-  }
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
+    for (int r = 0; r < 16; ++r) cw[r] = w[r][wi];
     float z[16];
+    auto unpack = [&]() {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (IN_BF16) {
-        const uint32_t v = w[r][j >> 1];
-        z[r] = (j & 1) ? bf16_hi(v) : bf16_lo(v);
-      } else {
-        z[r] = __uint_as_float(w[r][j]);
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+        const uint32_t v = cw[r] ^ sflip;
+        z[r] = IN_BF16 ? ((j & 1) ? bf16_hi(v) : bf16_lo(v)) : __uint_as_float(v);
       }
+    };
+    unpack();
+    // fast stages; the exact ones when the wave holds a zero output (the raw
+    // words pass through an empty asm so that the compiler recomputes the
+    // in-lane stages instead of keeping them alive from the fast path)
+    if (p.rht && fwht128_group_fast(z, lig)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(cw[r]));
+      unpack();
+      fwht128_group(z, lig);
     }
-    if (p.rht) fwht128_group(z, lig);
-    const uint32_t col = col0 + j;
-    const uint32_t kblk = tt * 8 + lig;
+    const uint32_t col = c0 + j;
     const bool active = rows_ok && col < p.cols;
     quant_block<MODE>(z, active ? col * p.K16 + kblk : 0u, active, p, s_t, lmax);
   }
@@ -432,7 +489,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   const uint32_t waves = gridDim.x * (kThreads / kWave);
   float lmax = 0.0f;
 
-  for (uint32_t t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6); t < p.ntiles; t += waves) {
+  for (uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6));
+       t < p.ntiles; t += waves) {
     const uint32_t tt = fdiv(t, p.ctiles_div);
     const uint32_t tc = t - tt * nct;
     col_tile<IN_BF16, MODE>(p, tt, tc, lig, q, sbits, s_t, lmax);
@@ -453,9 +511,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
 // its own partial maxima and target scales.
 template <int IN_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantParams pc) {
-  constexpr int CPL = IN_BF16 ? 2 * kColWords : kColWords;
-  constexpr int TCOL = 8 * CPL;
-  constexpr uint32_t kWidth = 4 * TCOL;      // tile columns
+  constexpr uint32_t kWidth = 4 * ColCfg<IN_BF16>::kTileCols;  // tile columns
   constexpr uint32_t kBpr = kWidth / 16;     // row blocks per tile row
   __shared__ float red[kThreads / kWave];
   float s_r = 1.0f, s_c = 1.0f;
@@ -488,8 +544,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
       RawBlock<IN_BF16> raw = {};
       if (active) load_row_block<IN_BF16>(pr, gb, raw);
       float z[16];
-      unpack_block<IN_BF16>(raw, sm, z);
-      if (pr.rht) fwht128_group(z, lig);
+      load_z<IN_BF16>(raw, sm, pr.rht, lig, z);
       quant_block<MODE>(z, active ? gb : 0u, active, pr, s_r, lmax_r);
     }
     // column-wise: wave w takes wave tile column 4 * tcw + w
@@ -591,7 +646,7 @@ hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, 
 }
 
 uint32_t dual_grid(const QuantParams &pr, int in_bf16) {
-  const uint32_t width = 4u * 8u * (in_bf16 ? 2u * kColWords : (uint32_t)kColWords);
+  const uint32_t width = 4u * (in_bf16 ? ColCfg<1>::kTileCols : ColCfg<0>::kTileCols);
   const uint64_t tiles = (uint64_t)(pr.rows / 128) * ((pr.cols + width - 1) / width);
   uint64_t g = tiles < 1 ? 1 : tiles;
   return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);

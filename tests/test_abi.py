@@ -95,6 +95,12 @@ def test_quantize_rejections(nv):
     assert _q(nv, ts=0) == INVALID
     assert _q(nv, x=FAKE + 8) == MISALIGNED
     assert _q(nv, ld=260, dtype=1) == MISALIGNED          # 520-byte rows
+    # axis 1: rows of up to 16 MiB pass the shape checks (and fail later, on
+    # the workspace); one element more is unsupported
+    assert _q(nv, rows=128, axis=1, ld=1 << 23, ws_bytes=100) == WS_SMALL
+    assert _q(nv, rows=128, axis=1, ld=(1 << 23) + 8, ws_bytes=100) == UNSUPPORTED
+    assert _q(nv, rows=128, axis=1, ld=1 << 22, dtype=0, ws_bytes=100) == WS_SMALL
+    assert _q(nv, rows=128, axis=1, ld=(1 << 22) + 4, dtype=0, ws_bytes=100) == UNSUPPORTED
     assert _q(nv, codes=FAKE + 4) == MISALIGNED
     assert _q(nv, ws=FAKE + 16) == MISALIGNED
     assert _q(nv, ws_bytes=100) == WS_SMALL

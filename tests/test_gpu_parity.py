@@ -245,6 +245,62 @@ def test_rht_signed_zero_cancellations(nv):
             assert_bit_exact(g, r, f"zero cancellations {name} axis{axis}")
 
 
+def _negative_zero_groups(signs, rows, cols, seed):
+    """bf16-exact input whose 128-groups are, by row: Gaussian; half of the
+    group -0 after the sign flips and the other half cancelling exactly (the
+    last butterfly then gives (-0) - (+0) = -0); the same at quarter scale;
+    all zeros of random signs.  The oracle's rotation of such groups has
+    outputs of both zero signs."""
+    rng = np.random.default_rng(seed)
+    flip = np.where(np.asarray(signs) > 0, -1.0, 1.0).astype(np.float32)
+    x = synth.to_bf16_f32(rng.standard_normal((rows, cols)).astype(np.float32))
+    for r in range(rows):
+        kind = r % 4
+        for g0 in range(0, cols, 128):
+            if kind == 0 or (g0 // 128 + r) % 3 == 0:
+                continue                                         # stays Gaussian
+            seg = np.empty(128, dtype=np.float32)
+            if kind == 3:
+                seg[:] = np.where(rng.integers(0, 2, 128) > 0, -0.0, 0.0)
+            else:
+                part = 64 if kind == 1 else 32
+                neg = -0.0 * flip                                # flip * neg = -0
+                alt = flip * np.where(np.arange(128) % 2 == 0, 1.0, -1.0).astype(np.float32) * 0.75
+                pos = (np.arange(128) // part) % 2 == 0
+                seg[:] = np.where(pos, neg, alt)
+            x[r, g0:g0 + 128] = seg
+    return x
+
+
+def test_rotation_negative_zero_outputs(nv):
+    """Rotated outputs that are -0 in the oracle come out -0 on the GPU too,
+    while other groups of the same waves take the fast stages: rotation
+    values, RTN, SR and MS-EDEN codes, rows, columns and both axes at once."""
+    import torch
+    rng = np.random.default_rng(34)
+    signs = synth.signs_from_rng(rng)
+    w = oracle.signs_words(signs)
+    x = _negative_zero_groups(signs, 128, 768, seed=35)
+    ref_rot = oracle.rht(x, w)
+    assert np.count_nonzero((ref_rot == 0) & np.signbit(ref_rot)) > 50
+    assert np.count_nonzero((ref_rot == 0) & ~np.signbit(ref_rot)) > 50
+    for axis in (0, 1):
+        xin = x if axis == 0 else np.ascontiguousarray(x.T)
+        z = nv.rht(to_device(xin, "bf16"), signs, axis=axis).cpu().numpy()
+        assert np.array_equal(z.view(np.uint32), ref_rot.view(np.uint32)), f"rotation axis{axis}"
+        for name, rnd in (("rtn", oracle.RTN), ("sr", oracle.SR), ("mseden", oracle.MSEDEN)):
+            g = q_to_host(nv.quantize_nvfp4(to_device(xin, "bf16"), rounding=name, axis=axis, rht_signs=signs,
+                                            seed=6, stream_id=2))
+            r = oracle.quantize(xin, rounding=rnd, axis=axis, rht_on=True, signs_w=w, seed=6, stream=2)
+            assert_bit_exact(g, r, f"-0 outputs {name} axis{axis}")
+    xt = x.T.copy()        # both axes at once quantize along the rows of their input
+    qr, qc = nv.quantize_nvfp4_dual(to_device(xt, "bf16"), rht_signs=signs, seed=8)
+    for axis, q in ((0, qr), (1, qc)):
+        r = oracle.quantize(xt, rounding=oracle.MSEDEN, axis=axis, rht_on=True, signs_w=w, seed=8)
+        assert_bit_exact(q_to_host(q), r, f"-0 outputs dual axis{axis}")
+    torch.cuda.synchronize()
+
+
 def test_tensor_scale_in(nv):
     import torch
     x = synth.gaussian(128, 512, seed=12)
