@@ -67,18 +67,64 @@ __device__ __forceinline__ void unpack_f32(const uint32_t w[16], const SignMasks
 
 __device__ __forceinline__ uint32_t sign_nib(float z) { return (__float_as_uint(z) >> 28) & 8u; }
 
-__device__ __forceinline__ void store_codes(const QuantParams &p, uint32_t gb, uint32_t lo,
-                                            uint32_t hi) {
-  *reinterpret_cast<uint2 *>(p.codes + (size_t)gb * 8) = make_uint2(lo, hi);
-}
+// ---------------------------------------------------------------- outputs
+// Where one block's results go.  PtrSink: plain stores, skipped by lanes
+// that hold no block.  RowSink: buffer stores over the blocks from `base` on,
+// whose range check drops the stores of lanes past the last block -- no
+// branch, so that every path through a loop iteration leaves the same
+// memory operations pending and the compiler's waits for the next block's
+// loads stay exact.
+struct PtrSink {
+  const QuantParams &p;
+  uint32_t gb;
+  bool active;
+  __device__ __forceinline__ void codes(uint32_t lo, uint32_t hi) const {
+    if (active) *reinterpret_cast<uint2 *>(p.codes + (size_t)gb * 8) = make_uint2(lo, hi);
+  }
+  __device__ __forceinline__ void scale(uint32_t e) const {
+    if (active) p.scales[gb] = (uint8_t)e;
+  }
+  __device__ __forceinline__ void target(float t) const {
+    if (active) p.tb[gb] = t;
+  }
+};
+
+struct RowSink {
+  __amdgpu_buffer_rsrc_t c, s, t;  // codes, scales, targets from block `base` on
+  uint32_t r;                       // this lane's block - base
+  bool active;
+  __device__ __forceinline__ RowSink(const QuantParams &p, uint32_t base, uint32_t rank) {
+    const uint64_t left = p.nblocks - base;  // blocks from base on (base < nblocks)
+    const int nc = (int)(8 * left < 0x7FFFFFFFull ? 8 * left : 0x7FFFFFFFull);
+    const int ns = (int)(left < 0x7FFFFFFFull ? left : 0x7FFFFFFFull);
+    const int nt = (int)(4 * left < 0x7FFFFFFFull ? 4 * left : 0x7FFFFFFFull);
+    c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.codes + (size_t)base * 8), (short)0, nc, kRsrcWord3);
+    s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.scales + base), (short)0, ns, kRsrcWord3);
+    t = __builtin_amdgcn_make_buffer_rsrc((void *)(p.tb ? p.tb + base : nullptr), (short)0, p.tb ? nt : 0,
+                                          kRsrcWord3);
+    r = rank;
+    active = base + rank < p.nblocks;
+  }
+  __device__ __forceinline__ void codes(uint32_t lo, uint32_t hi) const {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, c, 8 * r, 0, 0);
+  }
+  __device__ __forceinline__ void scale(uint32_t e) const {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, s, r, 0, 0);
+  }
+  __device__ __forceinline__ void target(float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), t, 4 * r, 0, 0);
+  }
+};
 
 // ---------------------------------------------------------------- one block
-// z: the lane's 16 (rotated) values; gb: block index in the output layout.
-// Must be called by every lane of a wave (the MS-EDEN correction of a
-// 128-group reduces over 8 lanes); `active` gates the stores.
-template <int MODE>
-__device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool active,
+// z: the lane's 16 (rotated) values; out: where its results go (out.gb for
+// PtrSink: block index in the output layout).  Must be called by every lane
+// of a wave (the MS-EDEN correction of a 128-group reduces over 8 lanes).
+template <int MODE, typename Sink>
+__device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink &out,
                                             const QuantParams &p, float s_t, float &lmax) {
+  const bool active = out.active;
   if constexpr (MODE == kRot) {
     if (active) {
       float4 *o = reinterpret_cast<float4 *>(p.rot_out + (size_t)gb * 16);
@@ -120,10 +166,8 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
           else hi |= nib << (4 * (i - 8));
         }
       }
-      if (active) {
-        store_codes(p, gb, lo, hi);
-        p.scales[gb] = (uint8_t)e;
-      }
+      out.codes(lo, hi);
+      out.scale(e);
     } else if constexpr (MODE == kIf4) {
       // both branches at their own scales; keep the smaller pairwise SSE.
       const uint32_t ef = e4m3_rne_sat(div_by<6>(a) / s_t);
@@ -152,10 +196,8 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
         else ihi |= (sn | mi) << (4 * (i - 8));
       }
       const bool use_int = tree16(sqi) < tree16(sqf);
-      if (active) {
-        store_codes(p, gb, use_int ? ilo : flo, use_int ? ihi : fhi);
-        p.scales[gb] = (uint8_t)(use_int ? (ei | 0x80u) : ef);
-      }
+      out.codes(use_int ? ilo : flo, use_int ? ihi : fhi);
+      out.scale(use_int ? (ei | 0x80u) : ef);
     } else if constexpr (MODE == kFos) {
       // Four Over Six: RTN with the block maximum mapped to 6 and to 4;
       // keep the smaller pairwise SSE (tie: 6).
@@ -185,10 +227,8 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
         sq4[i] = d * d;
       }
       const bool use4 = tree16(sq4) < tree16(sq6);
-      if (active) {
-        store_codes(p, gb, use4 ? lo4 : lo6, use4 ? hi4 : hi6);
-        p.scales[gb] = (uint8_t)(use4 ? e4 : e6);
-      }
+      out.codes(use4 ? lo4 : lo6, use4 ? hi4 : hi6);
+      out.scale(use4 ? e4 : e6);
     } else if constexpr (MODE == kSearch) {
       // RTN at the scale bytes e0, e0-1, e0+1, ..., e0-9, e0+9 (those in
       // 1..126; e0 always); keep the first strictly smaller pairwise SSE.
@@ -220,10 +260,8 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
           bhi = hi;
         }
       }
-      if (active) {
-        store_codes(p, gb, blo, bhi);
-        p.scales[gb] = (uint8_t)best_e;
-      }
+      out.codes(blo, bhi);
+      out.scale(best_e);
     } else if constexpr (MODE == kEden || MODE == kEdenFused) {
       // RTN codes under the exact scale a/6; correction c = sum z^2 /
       // sum z*zhat over the group; target t = (a/6) * c.
@@ -253,18 +291,14 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, bool activ
       const float c = (D > 0.0f) ? N / D : 1.0f;
       const float t = s_b * c;
       if constexpr (MODE == kEden) {
-        if (active) {
-          store_codes(p, gb, lo, hi);
-          p.tb[gb] = t;
-          lmax = fmaxf(lmax, t);
-        }
+        out.codes(lo, hi);
+        out.target(t);
+        if (active) lmax = fmaxf(lmax, t);
       } else {
         const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);
         const uint32_t e = e4m3_sr_sat(fminf(t / s_t, 448.0f), uniform_at(u, (int)(gb & 7u)));
-        if (active) {
-          store_codes(p, gb, lo, hi);
-          p.scales[gb] = (uint8_t)e;
-        }
+        out.codes(lo, hi);
+        out.scale(e);
       }
     }
   }
@@ -343,16 +377,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   // the next block's loads are issued before the current block is processed
   RawBlock<IN_BF16> cur = {}, nxt = {};
   uint32_t base = blockIdx.x * kThreads;
-  if (base + rank < p.nblocks) load_row_block<IN_BF16>(p, base + rank, cur);
+  // (loads past the last block re-read it, unconditionally: see RowSink)
+  if (base < p.nblocks) load_row_block<IN_BF16>(p, min(base + rank, p.nblocks - 1), cur);
   for (; base < p.nblocks; base += stride) {
     const uint32_t gb = base + rank;
     const bool active = gb < p.nblocks;
-    if (base + stride + rank < p.nblocks) load_row_block<IN_BF16>(p, base + stride + rank, nxt);
+    load_row_block<IN_BF16>(p, min(base + stride + rank, p.nblocks - 1), nxt);
     // lanes past the end hold stale values; they fill whole rotation groups
     // and store nothing, so they never reach an output
     float z[16];
     load_z<IN_BF16>(cur, sm, p.rht, lig, z);
-    quant_block<MODE>(z, gb, active, p, s_t, lmax);
+    if constexpr (MODE == kRot) quant_block<MODE>(z, gb, PtrSink{p, gb, active}, p, s_t, lmax);
+    else quant_block<MODE>(z, gb, RowSink(p, base, rank), p, s_t, lmax);
     cur = nxt;
   }
   if constexpr (MODE == kAmax || MODE == kEden) {
@@ -469,7 +505,8 @@ __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint
     }
     const uint32_t col = c0 + j;
     const bool active = rows_ok && col < p.cols;
-    quant_block<MODE>(z, active ? col * p.K16 + kblk : 0u, active, p, s_t, lmax);
+    const uint32_t gbc = active ? col * p.K16 + kblk : 0u;
+    quant_block<MODE>(z, gbc, PtrSink{p, gbc, active}, p, s_t, lmax);
   }
 }
 
@@ -545,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
       if (active) load_row_block<IN_BF16>(pr, gb, raw);
       float z[16];
       load_z<IN_BF16>(raw, sm, pr.rht, lig, z);
-      quant_block<MODE>(z, active ? gb : 0u, active, pr, s_r, lmax_r);
+      quant_block<MODE>(z, active ? gb : 0u, PtrSink{pr, active ? gb : 0u, active}, pr, s_r, lmax_r);
     }
     // column-wise: wave w takes wave tile column 4 * tcw + w
     col_tile<IN_BF16, MODE>(pc, tt, 4 * tcw + (threadIdx.x >> 6), lig, q, sbits, s_c, lmax_c);
