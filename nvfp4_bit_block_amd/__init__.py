@@ -187,7 +187,7 @@ def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, ten
         raise NvFp4Error("x must be 2-D")
     if not x.is_cuda:
         raise NvFp4Error("x must be a device tensor")
-    if x.stride(1) != 1:
+    if x.size(1) > 1 and x.stride(1) != 1:
         raise NvFp4Error("x must have unit stride along its last dimension")
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
@@ -230,7 +230,7 @@ def quantize_nvfp4_dual(x, rht_signs=None, seed=0, stream_id=0, eden_group=128, 
     rounding "mseden" and axis 0 / axis 1."""
     import torch
     L = lib()
-    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+    if x.dim() != 2 or not x.is_cuda or (x.size(1) > 1 and x.stride(1) != 1):
         raise NvFp4Error("x must be a 2-D device tensor with unit stride along its last dimension")
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols

@@ -610,26 +610,39 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     s_t = (m > 0.0f) ? m / 448.0f : 1.0f;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
-  const uint32_t ncalls = (p.nblocks + 7u) / 8u;
-  for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < ncalls; c += gridDim.x * kThreads) {
+  // Whole calls (8 blocks each): the next call's targets are loaded while
+  // this one is coded (clamped to the last call, so the load is unconditional).
+  const uint32_t nfull = p.nblocks / 8u;
+  const uint32_t stride = gridDim.x * kThreads;
+  auto code8 = [&](uint32_t c, const float4 &t0, const float4 &t1) {
     const Philox4 u = uniforms8(p.key, (uint64_t)c, 1u);
-    const uint32_t b0 = c * 8u;
-    if (b0 + 8u <= p.nblocks) {
-      const float4 t0 = *reinterpret_cast<const float4 *>(p.tb + b0);
-      const float4 t1 = *reinterpret_cast<const float4 *>(p.tb + b0 + 4);
-      const float t[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-      uint32_t lo = 0, hi = 0;
+    const float t[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t e = e4m3_sr_sat(fminf(t[j] / s_t, 448.0f), uniform_at(u, j));
-        if (j < 4) lo |= e << (8 * j);
-        else hi |= e << (8 * (j - 4));
-      }
-      *reinterpret_cast<uint2 *>(p.scales + b0) = make_uint2(lo, hi);
-    } else {
-      for (uint32_t j = 0; b0 + j < p.nblocks; ++j)
-        p.scales[b0 + j] = (uint8_t)e4m3_sr_sat(fminf(p.tb[b0 + j] / s_t, 448.0f), uniform_at(u, (int)j));
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = e4m3_sr_sat(fminf(t[j] / s_t, 448.0f), uniform_at(u, j));
+      if (j < 4) lo |= e << (8 * j);
+      else hi |= e << (8 * (j - 4));
     }
+    *reinterpret_cast<uint2 *>(p.scales + (size_t)c * 8) = make_uint2(lo, hi);
+  };
+  uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+  if (c < nfull) {
+    const float4 *tb = reinterpret_cast<const float4 *>(p.tb);
+    float4 a0 = tb[2 * (size_t)c], a1 = tb[2 * (size_t)c + 1];
+    for (; c < nfull; c += stride) {
+      const uint32_t cn = c + stride < nfull ? c + stride : nfull - 1;
+      const float4 n0 = tb[2 * (size_t)cn], n1 = tb[2 * (size_t)cn + 1];
+      code8(c, a0, a1);
+      a0 = n0;
+      a1 = n1;
+    }
+  }
+  // the last, partial call
+  if (p.nblocks % 8u && blockIdx.x * kThreads + threadIdx.x == nfull % stride) {
+    const Philox4 u = uniforms8(p.key, (uint64_t)nfull, 1u);
+    for (uint32_t j = 0; nfull * 8u + j < p.nblocks; ++j)
+      p.scales[nfull * 8u + j] = (uint8_t)e4m3_sr_sat(fminf(p.tb[nfull * 8u + j] / s_t, 448.0f), uniform_at(u, (int)j));
   }
 }
 

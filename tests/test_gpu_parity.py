@@ -358,6 +358,20 @@ def test_deterministic_replay(nv):
     assert not np.array_equal(a["codes"], c["codes"])
 
 
+@pytest.mark.parametrize("axis", [0, 1])
+def test_mseden_group16_block_count_not_multiple_of_8(nv, axis):
+    """MS-EDEN with 16-element groups on shapes whose block count is not a
+    multiple of 8: the scale pass codes the last, partial Philox call (and
+    a tensor below one call) like the rest."""
+    for i, (r, c) in enumerate([(37, 80), (5, 48), (1, 16), (261, 208)]):
+        x = synth.gradient(r, c, seed=900 + i)[0]
+        xin = x if axis == 0 else np.ascontiguousarray(x.T)
+        g = _run(nv, xin, "bf16", oracle.MSEDEN, axis, None, group=16)
+        ref = _ref(xin, oracle.MSEDEN, axis, None, group=16)
+        assert g["scales"].size % 8 != 0
+        assert_bit_exact(g, ref, f"eden16 axis{axis} {r}x{c}")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_columns_unaligned_rows_and_many_tiles(nv, dtype):
     """Column-wise quantization where every tile takes the element-wise path
