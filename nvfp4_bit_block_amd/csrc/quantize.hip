@@ -8,7 +8,8 @@
 // and the per-group FP4/INT4 selection.
 //
 // Work decomposition: one lane owns one 16-element block (one E4M3 scale) of
-// the OUTPUT layout; a 128-point rotation group is 8 consecutive lanes.
+// the OUTPUT layout; a 128-point rotation group is 8 lanes of one 16-lane
+// DPP row, holding 8 consecutive blocks.
 //   axis 0: a block is 16 contiguous input elements (two 16-byte loads for
 //           bf16), addressed by the flat block index.
 //   axis 1: a lane loads 16 rows of one 16-byte column chunk and so holds
