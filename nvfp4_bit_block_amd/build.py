@@ -73,5 +73,31 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_divcheck(verbose: bool = False) -> str:
+    """tests/_build/libdivcheck.so: the device check of the refined division
+    (test infrastructure; see tests/divcheck.hip)."""
+    tests = os.path.join(os.path.dirname(HERE), "tests")
+    out_dir = os.path.join(tests, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    so = os.path.join(out_dir, "libdivcheck.so")
+    obj = os.path.join(out_dir, "divcheck.o")
+    cmd = [_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(tests, "divcheck.hip"), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for divcheck.hip:\n{r.stdout}\n{r.stderr}")
+    tdir = _torch_lib_dir()
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    link = ["g++", "-shared", "-o", so + ".tmp", obj]
+    if tdir:
+        link += [f"-L{tdir}", "-l:libamdhip64.so", f"-Wl,-rpath,{tdir}"]
+    else:
+        link += [f"-L{rocm}/lib", "-lamdhip64", f"-Wl,-rpath,{rocm}/lib"]
+    subprocess.run(link, check=True)
+    os.replace(so + ".tmp", so)
+    return so
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

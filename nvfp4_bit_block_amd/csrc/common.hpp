@@ -42,12 +42,59 @@ template <int D>
 __device__ __forceinline__ float div_by(float a) {
   constexpr float d = (float)D;
   constexpr float inv = 1.0f / (float)D;
-  if (a >= 0x1p-119f) {
-    const float q0 = a * inv;
-    const float r = __builtin_fmaf(-q0, d, a);
-    return __builtin_fmaf(r, inv, q0);
-  }
-  return a / d;
+  const float q0 = a * inv;
+  const float r = __builtin_fmaf(-q0, d, a);
+  float q = __builtin_fmaf(r, inv, q0);
+  // (IEEE division below the range, when some lane of the wave needs it)
+  if (__builtin_amdgcn_ballot_w64(!(a >= 0x1p-119f)) != 0) q = (a >= 0x1p-119f) ? q : a / d;
+  return q;
+}
+
+// Correctly rounded reciprocal and quotient from the hardware reciprocal
+// v_rcp_f32 (error below one ulp), after Markstein (P. Markstein, "IA-64 and
+// Elementary Functions", Prentice Hall 2000, chapter 8):
+//   e  = 1 - b*y0        one fma, exact
+//   y1 = y0 + e*y0       one fma: the correctly rounded 1/b
+//   q0 = a*y1            within one ulp of a/b
+//   r  = a - b*q0        one fma, exact
+//   q1 = q0 + r*y1       one fma: the correctly rounded a/b (Markstein's
+//                        theorem, given y1 = RN(1/b))
+// One Newton step from a one-ulp seed is not proven to give RN(1/b) in
+// general: the device check (tests/divcheck.hip) compares y1 with the IEEE
+// reciprocal for every b of the range and q1 with the IEEE quotient for
+// every pair of significands.  Within [2^-60, 2^60] every intermediate is
+// normal and the steps scale exactly with the exponents; outside it (and
+// for NaN or infinite operands) the IEEE division runs.  Four (reciprocal)
+// and six (quotient) instructions instead of about ten.
+constexpr float kDivLo = 0x1p-60f, kDivHi = 0x1p60f;
+
+__device__ __forceinline__ float rcp_refined(float b) {
+  const float y0 = __builtin_amdgcn_rcpf(b);
+  const float e = __builtin_fmaf(-b, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
+// The IEEE operation runs only when some lane of the wave is outside the
+// range (one wave-uniform branch), so that the common path has no divergent
+// control flow to break the schedule.
+
+// 1/b.
+__device__ __forceinline__ float rcp_rn(float b) {
+  float y = rcp_refined(b);
+  const bool ok = b >= kDivLo && b <= kDivHi;
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) y = ok ? y : 1.0f / b;
+  return y;
+}
+
+// a/b.
+__device__ __forceinline__ float div_rn(float a, float b) {
+  const float y = rcp_refined(b);
+  const float q0 = a * y;
+  const float r = __builtin_fmaf(-b, q0, a);
+  float q = __builtin_fmaf(r, y, q0);
+  const bool ok = b >= kDivLo && b <= kDivHi && (a == 0.0f || (a >= kDivLo && a <= kDivHi));
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) q = ok ? q : a / b;
+  return q;
 }
 
 // ---------------------------------------------------------------- E4M3

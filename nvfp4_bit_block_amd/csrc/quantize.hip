@@ -143,9 +143,9 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
     } else if constexpr (MODE == kRtn || MODE == kSr) {
       // scale e = E4M3((a/6)/s_t), RNE (RTN) or rounded up (SR); codes of
       // min(|z| / (e * s_t), 6) on the E2M1 grid.
-      const float v = div_by<6>(a) / s_t;
+      const float v = div_rn(div_by<6>(a), s_t);
       const uint32_t e = (MODE == kRtn) ? e4m3_rne_sat(v) : e4m3_ceil_sat(v);
-      const float r = e ? 1.0f / (e4m3_value(e) * s_t) : 0.0f;
+      const float r = e ? rcp_rn(e4m3_value(e) * s_t) : 0.0f;
       Philox4 u0, u1;
       if constexpr (MODE == kSr) {
         u0 = uniforms8(p.key, (uint64_t)gb * 2u, 0u);
@@ -171,12 +171,12 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       out.scale(e);
     } else if constexpr (MODE == kIf4) {
       // both branches at their own scales; keep the smaller pairwise SSE.
-      const uint32_t ef = e4m3_rne_sat(div_by<6>(a) / s_t);
+      const uint32_t ef = e4m3_rne_sat(div_rn(div_by<6>(a), s_t));
       const float Sf = e4m3_value(ef) * s_t;
-      const float rf = ef ? 1.0f / Sf : 0.0f;
-      const uint32_t ei = e4m3_rne_sat(div_by<7>(a) / s_t);
+      const float rf = ef ? rcp_rn(Sf) : 0.0f;
+      const uint32_t ei = e4m3_rne_sat(div_rn(div_by<7>(a), s_t));
       const float Si = e4m3_value(ei) * s_t;
-      const float ri = ei ? 1.0f / Si : 0.0f;
+      const float ri = ei ? rcp_rn(Si) : 0.0f;
       float sqf[16], sqi[16], y[16], vf[16];
       uint32_t flo, fhi, ilo = 0, ihi = 0;
 #pragma unroll
@@ -202,12 +202,12 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
     } else if constexpr (MODE == kFos) {
       // Four Over Six: RTN with the block maximum mapped to 6 and to 4;
       // keep the smaller pairwise SSE (tie: 6).
-      const uint32_t e6 = e4m3_rne_sat(div_by<6>(a) / s_t);
+      const uint32_t e6 = e4m3_rne_sat(div_rn(div_by<6>(a), s_t));
       const float S6 = e4m3_value(e6) * s_t;
-      const float r6 = e6 ? 1.0f / S6 : 0.0f;
-      const uint32_t e4 = e4m3_rne_sat((a * 0.25f) / s_t);
+      const float r6 = e6 ? rcp_rn(S6) : 0.0f;
+      const uint32_t e4 = e4m3_rne_sat(div_rn(a * 0.25f, s_t));
       const float S4 = e4m3_value(e4) * s_t;
-      const float r4 = e4 ? 1.0f / S4 : 0.0f;
+      const float r4 = e4 ? rcp_rn(S4) : 0.0f;
       float y[16], v[16], sq6[16], sq4[16];
       uint32_t lo6, hi6, lo4, hi4;
 #pragma unroll
@@ -233,7 +233,7 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
     } else if constexpr (MODE == kSearch) {
       // RTN at the scale bytes e0, e0-1, e0+1, ..., e0-9, e0+9 (those in
       // 1..126; e0 always); keep the first strictly smaller pairwise SSE.
-      const int e0 = (int)e4m3_rne_sat(div_by<6>(a) / s_t);
+      const int e0 = (int)e4m3_rne_sat(div_rn(div_by<6>(a), s_t));
       uint32_t best_e = 0, blo = 0, bhi = 0;
       float best = 0.0f;
 #pragma unroll 1
@@ -241,7 +241,7 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
         const int e = e0 + (t + 1) / 2 * ((t & 1) ? -1 : 1);
         if (t > 0 && (e < 1 || e > 126)) continue;
         const float S = e4m3_value((uint32_t)e) * s_t;
-        const float r = e ? 1.0f / S : 0.0f;
+        const float r = e ? rcp_rn(S) : 0.0f;
         float y[16], v[16], sq[16];
         uint32_t lo, hi;
 #pragma unroll
@@ -267,7 +267,7 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       // RTN codes under the exact scale a/6; correction c = sum z^2 /
       // sum z*zhat over the group; target t = (a/6) * c.
       const float s_b = div_by<6>(a);
-      const float r = (a > 0.0f) ? 1.0f / s_b : 0.0f;
+      const float r = (a > 0.0f) ? rcp_rn(s_b) : 0.0f;
       float nn[16], dd[16], y[16], g[16];
       uint32_t lo, hi;
 #pragma unroll
@@ -289,7 +289,7 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
         N = N + lane_xor<4>(N);
         D = D + lane_xor<4>(D);
       }
-      const float c = (D > 0.0f) ? N / D : 1.0f;
+      const float c = (D > 0.0f) ? div_rn(N, D) : 1.0f;
       const float t = s_b * c;
       if constexpr (MODE == kEden) {
         out.codes(lo, hi);
@@ -297,7 +297,7 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
         if (active) lmax = fmaxf(lmax, t);
       } else {
         const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);
-        const uint32_t e = e4m3_sr_sat(fminf(t / s_t, 448.0f), uniform_at(u, (int)(gb & 7u)));
+        const uint32_t e = e4m3_sr_sat(fminf(div_rn(t, s_t), 448.0f), uniform_at(u, (int)(gb & 7u)));
         out.codes(lo, hi);
         out.scale(e);
       }
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t e = e4m3_sr_sat(fminf(t[j] / s_t, 448.0f), uniform_at(u, j));
+      const uint32_t e = e4m3_sr_sat(fminf(div_rn(t[j], s_t), 448.0f), uniform_at(u, j));
       if (j < 4) lo |= e << (8 * j);
       else hi |= e << (8 * (j - 4));
     }
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
   if (p.nblocks % 8u && blockIdx.x * kThreads + threadIdx.x == nfull % stride) {
     const Philox4 u = uniforms8(p.key, (uint64_t)nfull, 1u);
     for (uint32_t j = 0; nfull * 8u + j < p.nblocks; ++j)
-      p.scales[nfull * 8u + j] = (uint8_t)e4m3_sr_sat(fminf(p.tb[nfull * 8u + j] / s_t, 448.0f), uniform_at(u, (int)j));
+      p.scales[nfull * 8u + j] = (uint8_t)e4m3_sr_sat(fminf(div_rn(p.tb[nfull * 8u + j], s_t), 448.0f), uniform_at(u, (int)j));
   }
 }
 
