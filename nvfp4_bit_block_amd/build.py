@@ -54,10 +54,25 @@ def _compile(src, verbose):
     return obj
 
 
+def _device_asm(src, verbose):
+    """gfx950 assembly of one source, kept in _build/ for the build checks."""
+    out = os.path.join(BUILD, os.path.basename(src) + ".s")
+    cmd = [_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S",
+                                     os.path.join(CSRC, src), "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES) + 1)) as ex:
+        asm = ex.submit(_device_asm, "quantize.hip", verbose)
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        asm.result()
     tdir = _torch_lib_dir()
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     link = ["g++", "-shared", "-o", LIB + ".tmp"] + objs

@@ -378,11 +378,13 @@ __device__ __forceinline__ void fwht128_group(float v[16], uint32_t pos) {
 // The compiler does not fuse a DPP move into v_fmac_f32, so the stage is
 // written out: v_fmac_f32_dpp d, d, k computes d + k * (d of the partner
 // lane) -- every lane reads its partner's d before any lane writes.  The
-// leading s_nop 4 gives the wait states that a DPP read needs after a vector
-// write of its source register (2) or of EXEC (5); inside the block no
-// instruction reads a register that an earlier one wrote.
+// leading s_nop 1 gives the two wait states that a DPP read needs after a
+// vector write of its source register; inside the block no instruction
+// reads a register that an earlier one wrote.  (A DPP read also needs five
+// after a vector-ALU write of EXEC, v_cmpx; the library emits none, which
+// tests/test_build_invariants.py checks in the built assembly.)
 #define NV4_FMAC_DPP16(CTRL)                                                                      \
-  "s_nop 4\n\t"                                                                                   \
+  "s_nop 1\n\t"                                                                                   \
   "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
   "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
   "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t"                           \
