@@ -119,9 +119,10 @@ struct RowSink {
 };
 
 // ---------------------------------------------------------------- one block
-// z: the lane's 16 (rotated) values; out: where its results go (out.gb for
-// PtrSink: block index in the output layout).  Must be called by every lane
-// of a wave (the MS-EDEN correction of a 128-group reduces over 8 lanes).
+// z: the lane's 16 (rotated) values; gb: its block index in the output
+// layout (it keys the random numbers); out: where the results go.  Must be
+// called by every lane of a wave (the MS-EDEN correction of a 128-group
+// reduces over 8 lanes).
 template <int MODE, typename Sink>
 __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink &out,
                                             const QuantParams &p, float s_t, float &lmax) {
@@ -354,7 +355,8 @@ __device__ __forceinline__ void load_z(const RawBlock<IN_BF16> &b, const SignMas
     // keep the in-lane stages' results alive from the fast path for reuse)
     RawBlock<IN_BF16> c = b;
 #pragma unroll
-    for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) asm volatile("" : "+v"(c.q[i].x), "+v"(c.q[i].y), "+v"(c.q[i].z), "+v"(c.q[i].w));
+    for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i)
+      asm volatile("" : "+v"(c.q[i].x), "+v"(c.q[i].y), "+v"(c.q[i].z), "+v"(c.q[i].w));
     unpack_block<IN_BF16>(c, sm, z);
     fwht128_group(z, lig);
   }
