@@ -13,18 +13,19 @@
 // -- and multiplied on the fp16 matrix cores (v_mfma_f32_32x32x16_f16) with
 // fp32 accumulation.
 //
-// Tiling: a workgroup of 8 waves (two per SIMD, so that one can issue while
-// the other waits on LDS or the barrier) computes a 256 x 256 tile; wave
-// (wm, wn) a 64 x 128 sub-tile as 2 x 4 MFMA tiles of 32 x 32 (128 fp32
-// accumulators per lane).  K advances in chunks of 64 (four 16-wide MFMA
-// steps).  The tile's 16 row fragments per chunk (8 of A, 8 of B, 32 rows
-// each) are split between the waves: wave w loads fragment w of A and of B
-// (buffer loads; rows past M or N read as zero), dequantizes them once, and
-// writes the fp16 MFMA operands to LDS in operand order (lane l's 16 bytes at
-// slot l: conflict-free).  Every wave then reads its 2 + 4 operands per step
-// from LDS.  So each fragment is loaded and dequantized once per workgroup, not
-// once per wave that uses it -- the dequantization is the vector-ALU cost
-// that competes with the matrix cores.  LDS is double-buffered (2 x 64 KB):
+// Tiling: a workgroup of 16 waves (four per SIMD, so that others can issue
+// while one waits on LDS or the barrier) computes a 256 x 256 tile; wave
+// (wm, wn) a 64 x 64 sub-tile as 2 x 2 MFMA tiles of 32 x 32 (64 fp32
+// accumulators per lane, 118 VGPRs in all).  K advances in chunks of 64
+// (four 16-wide MFMA steps).  The tile's 16 row fragments per chunk (8 of A,
+// 8 of B, 32 rows each) are split between the waves: wave w loads fragment w
+// (A for w < 8, B after; buffer loads, rows past M or N read as zero),
+// dequantizes it once, and writes the fp16 MFMA operands to LDS in operand
+// order (lane l's 16 bytes at slot l: conflict-free).  Every wave then reads
+// its 2 + 2 operands per step from LDS.  So each fragment is loaded and
+// dequantized once per workgroup, not once per wave that uses it -- the
+// dequantization is the vector-ALU cost that competes with the matrix
+// cores.  LDS is double-buffered (2 x 64 KB):
 // chunk c+1 is dequantized, one step at a time, between the MFMA steps of
 // chunk c, and the raw codes of chunk c+3 are loaded as soon as a register
 // buffer frees up; one barrier per chunk.
@@ -47,60 +48,47 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kTile = 256, kWaveCols = 128, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
+constexpr uint32_t kTile = 256, kWaveCols = 64, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
 
-// Raw codes of this wave's 2 fragments for one chunk (own fragment 0 = A,
-// 1 = B): the lane's 32 codes and the chunk's four E4M3 scale bytes of its
-// row -- bytes 2h, 2h+1 are the lane half's.
+// Raw codes of this wave's fragment for one chunk: the lane's 32 codes and
+// the chunk's four E4M3 scale bytes of its row -- bytes 2h, 2h+1 are the
+// lane half's.
 struct Raw {
-  u32x4_t code[2];
-  uint32_t scale[2];
+  u32x4_t code;
+  uint32_t scale;
 };
 
 struct Panels {
-  __amdgpu_buffer_rsrc_t ac, as, bc, bs;  // codes / scales of this tile's rows
-  // vo_c: byte offset of this lane's row of its own fragments (the same row
-  // index in A and in B) plus its lane half's first code byte; vo_s: that
-  // row's first scale byte.  The whole row offset is in the vector offset, so
+  __amdgpu_buffer_rsrc_t c, s;  // codes / scales of the panel (A or B) of this wave's fragment
+  // vo_c: byte offset of this lane's row of its fragment plus its lane
+  // half's first code byte; vo_s: that row's first scale byte.  The whole row offset is in the vector offset, so
   // rows past M or N fall outside the buffer's range and read as zero; the
   // chunk's k offset (< one row) is the scalar offset.
   uint32_t vo_c, vo_s;
   uint32_t K, h;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_c(const Panels &p, int o) { return o < 1 ? p.ac : p.bc; }
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t own_rsrc_s(const Panels &p, int o) { return o < 1 ? p.as : p.bs; }
-
 // Whole chunk at k0 < K, K % 64 == 0.
 __device__ __forceinline__ void load_fast(Raw &r, const Panels &p, uint32_t k0) {
-#pragma unroll
-  for (int o = 0; o < 2; ++o) {
-    r.code[o] = __builtin_amdgcn_raw_buffer_load_b128(own_rsrc_c(p, o), p.vo_c, k0 / 2, 0);
-    r.scale[o] = __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_s(p, o), p.vo_s, k0 / 16, 0);
-  }
+  r.code = __builtin_amdgcn_raw_buffer_load_b128(p.c, p.vo_c, k0 / 2, 0);
+  r.scale = __builtin_amdgcn_raw_buffer_load_b32(p.s, p.vo_s, k0 / 16, 0);
 }
 
 // Any chunk at k0 < K, K % 16 == 0: dword- and byte-granular loads, zero past K.
 __device__ __forceinline__ void load_generic(Raw &r, const Panels &p, uint32_t k0) {
   const uint32_t kl = k0 + 32 * p.h;  // first k of this lane's 32
+  uint32_t w[4];
 #pragma unroll
-  for (int o = 0; o < 2; ++o) {
-    uint32_t w[4];
+  for (int q = 0; q < 4; ++q)
+    w[q] = (kl + 8 * q + 8 <= p.K) ? __builtin_amdgcn_raw_buffer_load_b32(p.c, p.vo_c + 4 * q, k0 / 2, 0) : 0u;
+  r.code = u32x4_t{w[0], w[1], w[2], w[3]};
+  uint32_t s = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = (kl + 8 * q + 8 <= p.K)
-                 ? __builtin_amdgcn_raw_buffer_load_b32(own_rsrc_c(p, o), p.vo_c + 4 * q, k0 / 2, 0)
-                 : 0u;
-    r.code[o] = u32x4_t{w[0], w[1], w[2], w[3]};
-    uint32_t s = 0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (kl + 16 * q < p.K)
-        s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(own_rsrc_s(p, o), p.vo_s + 2 * p.h + q,
-                                                            k0 / 16, 0)
-             << (8 * (q + 2 * p.h));
-    r.scale[o] = s;
-  }
+  for (int q = 0; q < 2; ++q)
+    if (kl + 16 * q < p.K)
+      s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(p.s, p.vo_s + 2 * p.h + q, k0 / 16, 0)
+           << (8 * (q + 2 * p.h));
+  r.scale = s;
 }
 
 // 8 codes (element 2i in the low nibble of byte i) times one fp16 scale.
@@ -152,56 +140,52 @@ typedef half8_t Stage[2][16][kSteps][64];
 // and, for IF4 operands, their INT flags (bits 7 and 15 of f).
 template <int IF4>
 struct Scales {
-  half2_t s[2];
-  uint32_t f[2];
+  half2_t s;
+  uint32_t f;
 };
 
 template <int IF4>
 __device__ __forceinline__ void scales16(const Raw &r, uint32_t h, Scales<IF4> &sc) {
-#pragma unroll
-  for (int o = 0; o < 2; ++o) {
-    const uint32_t b = r.scale[o] >> (16 * h);
-    if (IF4) {
-      sc.f[o] = b;
-      sc.s[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b & 0x7F7Fu, 1.0f, false);
-    } else {
-      sc.s[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
-    }
+  const uint32_t b = r.scale >> (16 * h);
+  if (IF4) {
+    sc.f = b;
+    sc.s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b & 0x7F7Fu, 1.0f, false);
+  } else {
+    sc.s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
   }
 }
 
-// Dequantize item q = 2 * step + own fragment (0..7) of a chunk into buffer b.
+// Dequantize step j of this wave's fragment (fragment w: A 0..7, B 8..15)
+// for one chunk into buffer b.
 template <int IF4>
 __device__ __forceinline__ void dequant_item(Stage &st, int b, const Raw &r, const Scales<IF4> &sc, uint32_t w,
-                                             uint32_t lane, int q) {
-  const int j = q >> 1, o = q & 1;
-  const int frag = o == 0 ? (int)w : 8 + (int)w;
+                                             uint32_t lane, int j) {
   if (IF4) {
-    const bool is_int = (sc.f[o] >> (8 * (j >> 1) + 7)) & 1u;
-    st[b][frag][j][lane] = dequant8_lut(r.code[o][j], sc.s[o][j >> 1], is_int ? kLutIntLo : kLutFpLo,
-                                        is_int ? kLutIntHi : kLutFpHi);
+    const bool is_int = (sc.f >> (8 * (j >> 1) + 7)) & 1u;
+    st[b][w][j][lane] = dequant8_lut(r.code[j], sc.s[j >> 1], is_int ? kLutIntLo : kLutFpLo,
+                                     is_int ? kLutIntHi : kLutFpHi);
   } else {
-    st[b][frag][j][lane] = dequant8(r.code[o][j], sc.s[o][j >> 1]);
+    st[b][w][j][lane] = dequant8(r.code[j], sc.s[j >> 1]);
   }
 }
 
 struct Ops {
-  half8_t a[2], b[4];
+  half8_t a[2], b[2];
 };
 
 __device__ __forceinline__ void read_ops(Ops &op, const Stage &st, int b, uint32_t wm, uint32_t wn, uint32_t lane,
                                          int j) {
 #pragma unroll
-  for (int n = 0; n < 4; ++n) op.b[n] = st[b][8 + 4 * wn + n][j][lane];
+  for (int n = 0; n < 2; ++n) op.b[n] = st[b][8 + 2 * wn + n][j][lane];
 #pragma unroll
   for (int m = 0; m < 2; ++m) op.a[m] = st[b][2 * wm + m][j][lane];
 }
 
-__device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[2][4]) {
+__device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[2][2]) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
       acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op.a[m], op.b[n], acc[m][n], 0, 0, 0);
 }
 
@@ -210,7 +194,7 @@ __device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[2][4]) {
 template <int NV>
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
     __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);   // LDS
@@ -219,14 +203,15 @@ __device__ __forceinline__ void interleave_step() {
 
 // One chunk of the steady state.  On entry `op` holds step 0 of chunk c (in
 // buffer c&1) and `rd` the raw codes of chunk c+1.  Steps 0-2 dequantize
-// chunk c+1 into the other buffer while computing; the barrier after step 2
-// publishes it (and retires every read of this chunk's buffer), so step 3
-// can already fetch chunk c+1's first operands.  `rd` is then reloaded with
+// chunk c+1 (two, one and one of its four steps) into the other buffer while
+// computing; the barrier after step 2 publishes it (and retires every read
+// of this chunk's buffer), so step 3 can already fetch chunk c+1's first
+// operands.  `rd` is then reloaded with
 // chunk `k_next` (clamped into range by the caller).
 template <int IF4>
 __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Raw &rd, Ops &op, const Panels &p,
                                       uint32_t w, uint32_t wm, uint32_t wn, uint32_t lane,
-                                      float16_t (&acc)[2][4]) {
+                                      float16_t (&acc)[2][2]) {
   const int cur = c & 1, nxt = cur ^ 1;
   Scales<IF4> s;
   scales16<IF4>(rd, p.h, s);
@@ -234,21 +219,19 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
   // step 0
   read_ops(nx, st, cur, wm, wn, lane, 1);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
+  for (int j = 0; j < 2; ++j) dequant_item<IF4>(st, nxt, rd, s, w, lane, j);
   mfma16(op, acc);
   interleave_step<IF4 ? 10 : 8>();
   __builtin_amdgcn_sched_barrier(0);
   // step 1
   read_ops(op, st, cur, wm, wn, lane, 2);
-#pragma unroll
-  for (int q = 3; q < 6; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
+  dequant_item<IF4>(st, nxt, rd, s, w, lane, 2);
   mfma16(nx, acc);
   interleave_step<IF4 ? 10 : 8>();
   __builtin_amdgcn_sched_barrier(0);
   // step 2
   read_ops(nx, st, cur, wm, wn, lane, 3);
-#pragma unroll
-  for (int q = 6; q < 8; ++q) dequant_item<IF4>(st, nxt, rd, s, w, lane, q);
+  dequant_item<IF4>(st, nxt, rd, s, w, lane, 3);
   mfma16(op, acc);
   interleave_step<IF4 ? 10 : 8>();
   __builtin_amdgcn_sched_barrier(0);
@@ -262,7 +245,7 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
 }
 
 template <int OUT_BF16, int FAST, int IF4>
-__global__ __launch_bounds__(512, 1) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
   __shared__ Stage st;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & 63u;
@@ -283,30 +266,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams p) {
   const uint32_t K = p.K, K2 = K / 2, K16 = K / 16;
   const uint32_t m0 = tm * kTile, n0 = tn * kTile;
   const uint32_t rows_a = min(kTile, p.M - m0), rows_b = min(kTile, p.N - n0);
-  const uint32_t wm = w >> 1, wn = w & 1u;   // wave tile: rows 64 wm.., columns 128 wn..
+  const uint32_t wm = w >> 2, wn = w & 3u;   // wave tile: rows 64 wm.., columns 64 wn..
 
   Panels P;
-  P.ac = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_codes + (size_t)m0 * K2), (short)0,
-                                           (int)(rows_a * K2), kRsrcWord3);
-  P.as = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_scales + (size_t)m0 * K16), (short)0,
-                                           (int)(rows_a * K16), kRsrcWord3);
-  P.bc = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_codes + (size_t)n0 * K2), (short)0,
-                                           (int)(rows_b * K2), kRsrcWord3);
-  P.bs = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_scales + (size_t)n0 * K16), (short)0,
-                                           (int)(rows_b * K16), kRsrcWord3);
+  if (w < 8) {
+    P.c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_codes + (size_t)m0 * K2), (short)0,
+                                            (int)(rows_a * K2), kRsrcWord3);
+    P.s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_scales + (size_t)m0 * K16), (short)0,
+                                            (int)(rows_a * K16), kRsrcWord3);
+  } else {
+    P.c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_codes + (size_t)n0 * K2), (short)0,
+                                            (int)(rows_b * K2), kRsrcWord3);
+    P.s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_scales + (size_t)n0 * K16), (short)0,
+                                            (int)(rows_b * K16), kRsrcWord3);
+  }
   {
-    const uint32_t row = 32 * w + r32;  // this lane's row of own fragments (A and B)
+    const uint32_t row = 32 * (w & 7u) + r32;  // this lane's row of its fragment
     P.vo_c = row * K2 + 16 * h;
     P.vo_s = row * K16;
   }
   P.K = K;
   P.h = h;
 
-  float16_t acc[2][4];
+  float16_t acc[2][2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.0f;
 
@@ -326,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams p) {
       Scales<IF4> s;
       scales16<IF4>(r0, P.h, s);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dequant_item<IF4>(st, 0, r0, s, w, lane, q);
+      for (int j = 0; j < 4; ++j) dequant_item<IF4>(st, 0, r0, s, w, lane, j);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_fast(r0, P, min(2 * kChunk, klast));
@@ -351,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams p) {
     Scales<IF4> s;
     scales16<IF4>(r, P.h, s);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dequant_item<IF4>(st, 0, r, s, w, lane, q);
+    for (int j = 0; j < 4; ++j) dequant_item<IF4>(st, 0, r, s, w, lane, j);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < (int)kSteps; ++j) {
@@ -368,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams p) {
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < 2; ++n) {
       const uint32_t col = n0 + wn * kWaveCols + 32 * n + r32;
       if (col >= p.N) continue;
 #pragma unroll
@@ -392,11 +378,11 @@ template <int IF4>
 static void launch_fmt(const GemmParams &p, int out_bf16, uint32_t tiles, hipStream_t s) {
   const bool fast = (p.K % 64) == 0;
   if (out_bf16) {
-    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(tiles), dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(tiles), dim3(512), 0, s, p);
+    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(tiles), dim3(1024), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(tiles), dim3(1024), 0, s, p);
   } else {
-    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(tiles), dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(tiles), dim3(512), 0, s, p);
+    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(tiles), dim3(1024), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(tiles), dim3(1024), 0, s, p);
   }
 }
 
