@@ -209,6 +209,15 @@ def main():
     ]
     outs = {n: qt(r, k) for n, _, _, _, _, r, k in plan}
     wss = {n: ws_for(x.shape[0], x.shape[1], rnd, ax) for n, x, rnd, ax, _, _, _ in plan}
+    # X and W are quantized column-wise (for the gradients) before their
+    # row-wise RTN (for Y): each column-wise MS-EDEN pass also writes max|x|,
+    # the row-wise RTN's tensor scale takes it, and X and W are read once
+    # less than with a separate maximum pass.
+    amax = {"X": torch.zeros(1, dtype=torch.float32, device=dev),
+            "W": torch.zeros(1, dtype=torch.float32, device=dev)}
+    handoff = {"qXc": {"amax_out": amax["X"]}, "qWc": {"amax_out": amax["W"]},
+               "qX": {"amax_in": amax["X"]}, "qW": {"amax_in": amax["W"]}}
+    by_name = {e[0]: e for e in plan}
     Y = torch.empty((T, O), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((O, D), dtype=torch.float32, device=dev)
@@ -217,7 +226,7 @@ def main():
 
     def quantize(name, x, rnd, ax, sg, step):
         nv.quantize_nvfp4(x, rounding=rnd, axis=ax, rht_signs=sg, seed=1000 + len(name), stream_id=step,
-                          out=outs[name], workspace=wss[name])
+                          out=outs[name], workspace=wss[name], **handoff.get(name, {}))
 
     ev_pool = []
 
@@ -229,27 +238,25 @@ def main():
 
     def step(i, timed):
         marks = []
-        for n, x, rnd, ax, sg, _, _ in plan[:2]:
+
+        def q(names):
+            for n in names:
+                _, x, rnd, ax, sg, _, _ = by_name[n]
+                a = ev() if timed else None
+                quantize(n, x, rnd, ax, sg, i)
+                marks.append(("q", n, a, ev() if timed else None))
+
+        def g(name, qa, qb, out):
             a = ev() if timed else None
-            quantize(n, x, rnd, ax, sg, i)
-            marks.append(("q", n, a, ev() if timed else None))
-        a = ev() if timed else None
-        nv.gemm_nvfp4(outs["qX"], outs["qW"], out=Y)
-        marks.append(("g", "Y", a, ev() if timed else None))
-        for n, x, rnd, ax, sg, _, _ in plan[2:4]:
-            a = ev() if timed else None
-            quantize(n, x, rnd, ax, sg, i)
-            marks.append(("q", n, a, ev() if timed else None))
-        a = ev() if timed else None
-        nv.gemm_nvfp4(outs["qdYr"], outs["qWc"], out=dX)
-        marks.append(("g", "dX", a, ev() if timed else None))
-        for n, x, rnd, ax, sg, _, _ in plan[4:6]:
-            a = ev() if timed else None
-            quantize(n, x, rnd, ax, sg, i)
-            marks.append(("q", n, a, ev() if timed else None))
-        a = ev() if timed else None
-        nv.gemm_nvfp4(outs["qdYc"], outs["qXc"], out=dW)
-        marks.append(("g", "dW", a, ev() if timed else None))
+            nv.gemm_nvfp4(outs[qa], outs[qb], out=out)
+            marks.append(("g", name, a, ev() if timed else None))
+
+        q(("qXc", "qWc", "qX", "qW"))     # column-wise first: they hand max|x| on
+        g("Y", "qX", "qW", Y)
+        q(("qdYr",))
+        g("dX", "qdYr", "qWc", dX)
+        q(("qdYc",))
+        g("dW", "qdYc", "qXc", dW)
         return marks
 
     if args.copy_calibration > 0:
@@ -322,7 +329,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "mlp_up_projection_training_step", "X": [T, D], "W": [O, D],
                    "dY": [T, O], "input_dtype": "bf16", "rotation": 128,
-                   "quantizations": "RTN(X,W) fwd; RHT+MS-EDEN(dY row+col, W col, X col) bwd",
+                   "quantizations": "RTN(X,W) fwd; RHT+MS-EDEN(dY row+col, W col, X col) bwd; "
+                                    "X, W col first, handing max|x| to their row RTN",
                    "gemms": "Y=XW^T (bf16), dX=dY W (bf16), dW=dY^T X (fp32)"},
         "hbm_frac": round(q_gbs / HBM_PEAK_GBS, 3),
         "gemm": {"value": round(g_tflops, 1), "unit": "TFLOP/s",

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -109,10 +109,19 @@ typedef struct nvfp4_opts {
   const float *tensor_scale_in; /* DEVICE pointer to a given fp32 tensor scale,
                               or NULL to compute it from this tensor           */
   int32_t scale_rule;      /* nvfp4_scale_rule; other than MAX6 needs RTN      */
+  float *amax_out;         /* DEVICE fp32 or NULL.  MS-EDEN with a computed
+                              tensor scale also writes max|x| of the input as
+                              given (before any rotation) here.               */
+  const float *amax_in;    /* DEVICE fp32 or NULL.  A call without rotation
+                              and without tensor_scale_in, other than MS-EDEN,
+                              takes max|x| from here instead of reading the
+                              input an extra time: s_t = amax_in / (6 * 448),
+                              or / (6 * 256) for Four Over Six, 1 if it is 0. */
 } nvfp4_opts;
 
 /* Fills *o with defaults: RTN, axis 0, no rotation, seed 0, stream 0,
- * eden_group 128, computed tensor scale, scale rule NVFP4_SCALE_MAX6. */
+ * eden_group 128, computed tensor scale, scale rule NVFP4_SCALE_MAX6, no
+ * amax_out / amax_in. */
 void nvfp4_opts_init(nvfp4_opts *o);
 
 /* Bytes of device workspace the quantizers need for this shape and options
@@ -162,6 +171,17 @@ size_t nvfp4_workspace_size(int64_t rows, int64_t cols, const nvfp4_opts *o);
  * given).  ws: device workspace of at least nvfp4_workspace_size() bytes,
  * 256-byte aligned; its contents on entry are ignored.
  * Shape rules: K % 16 == 0; K % 128 == 0 with rotation or MS-EDEN group 128.
+ * Tensor maximum handed between calls (the training step quantizes X and W
+ * row-wise for the forward product and column-wise for the weight and input
+ * gradients; the maximum the tensor scale of the row-wise RTN needs is a
+ * by-product of the column-wise MS-EDEN pass over the same tensor):
+ * o->amax_out (MS-EDEN, tensor scale computed) receives max|x|, ready when
+ * the call's work on the stream is; o->amax_in (no rotation, no
+ * tensor_scale_in, not MS-EDEN) replaces the pass that finds it -- the
+ * results are those of the call without it when *amax_in is the input's
+ * max|x|.  Other combinations: NVFP4_UNSUPPORTED; either pointer not 4-byte
+ * aligned: NVFP4_MISALIGNED.  An empty tensor writes 0 to amax_out and takes
+ * the tensor scale 1 whatever amax_in holds.
  */
 int nvfp4_quantize_nvfp4(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
                          const nvfp4_opts *o, uint8_t *codes, uint8_t *scales,

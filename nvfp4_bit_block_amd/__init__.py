@@ -48,6 +48,8 @@ class _Opts(ctypes.Structure):
         ("eden_group", ctypes.c_int32),
         ("tensor_scale_in", ctypes.c_void_p),
         ("scale_rule", ctypes.c_int32),
+        ("amax_out", ctypes.c_void_p),
+        ("amax_in", ctypes.c_void_p),
     ]
 
 
@@ -136,7 +138,8 @@ _SCALE_RULE = {"max6": SCALE_MAX6, "4over6": SCALE_4OVER6, "four_over_six": SCAL
                SCALE_SEARCH: SCALE_SEARCH}
 
 
-def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule=SCALE_MAX6):
+def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule=SCALE_MAX6,
+          amax_out=None, amax_in=None):
     o = _Opts()
     lib().nvfp4_opts_init(ctypes.byref(o))
     o.rounding = _ROUNDING[rounding.lower() if isinstance(rounding, str) else rounding]
@@ -151,6 +154,8 @@ def _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_i
     o.eden_group = int(eden_group)
     o.tensor_scale_in = None if tensor_scale_in is None else tensor_scale_in.data_ptr()
     o.scale_rule = _SCALE_RULE[scale_rule.lower() if isinstance(scale_rule, str) else scale_rule]
+    o.amax_out = None if amax_out is None else amax_out.data_ptr()
+    o.amax_in = None if amax_in is None else amax_in.data_ptr()
     return o
 
 
@@ -180,7 +185,7 @@ def workspace_size(rows, cols, rounding=RTN, axis=0, tensor_scale_in=None):
 
 
 def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in,
-              out, workspace, fmt, scale_rule=SCALE_MAX6):
+              out, workspace, fmt, scale_rule=SCALE_MAX6, amax_out=None, amax_in=None):
     import torch
     L = lib()
     if x.dim() != 2:
@@ -191,7 +196,11 @@ def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, ten
         raise NvFp4Error("x must have unit stride along its last dimension")
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
-    o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule)
+    for t in (amax_out, amax_in):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or t.numel() < 1):
+            raise NvFp4Error("amax_out / amax_in must be float32 device tensors of at least one element")
+    o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule,
+              amax_out, amax_in)
     R, K = (rows, cols) if axis == 0 else (cols, rows)
     dev = x.device
     if out is None:
@@ -212,14 +221,18 @@ def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, ten
 
 
 def quantize_nvfp4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0, eden_group=128,
-                   tensor_scale_in=None, out=None, workspace=None, scale_rule=SCALE_MAX6):
+                   tensor_scale_in=None, out=None, workspace=None, scale_rule=SCALE_MAX6,
+                   amax_out=None, amax_in=None):
     """NVFP4 quantization of a 2-D float32/bfloat16 device tensor (see
     ``nvfp4_quantize_nvfp4`` in include/nvfp4.h).  rht_signs: 128 flags or 4
     words enable the randomized Hadamard rotation.  scale_rule "4over6"
     selects Four Over Six block scaling, "search" a searched block scale
-    (both RTN only).  Returns a QTensor."""
+    (both RTN only).  amax_out (MS-EDEN) receives max|x|; amax_in (no
+    rotation, not MS-EDEN) supplies it instead of a pass over x: float32
+    device tensors.  Returns a QTensor."""
     return _quantize(lib().nvfp4_quantize_nvfp4, x, rounding, axis, rht_signs, seed, stream_id,
-                     eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4, scale_rule)
+                     eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4, scale_rule,
+                     amax_out, amax_in)
 
 
 def quantize_nvfp4_dual(x, rht_signs=None, seed=0, stream_id=0, eden_group=128, tensor_scale_in=None,
@@ -262,10 +275,10 @@ def workspace_size_dual(rows, cols, eden_group=128, tensor_scale_in=None):
     return int(lib().nvfp4_workspace_size_dual(int(rows), int(cols), ctypes.byref(o)))
 
 
-def quantize_if4(x, axis=0, rht_signs=None, tensor_scale_in=None, out=None, workspace=None):
+def quantize_if4(x, axis=0, rht_signs=None, tensor_scale_in=None, out=None, workspace=None, amax_in=None):
     """IF4 quantization (per-16 FP4/INT4 choice by lower squared error)."""
     return _quantize(lib().nvfp4_quantize_if4, x, RTN, axis, rht_signs, 0, 0, 128, tensor_scale_in,
-                     out, workspace, FORMAT_IF4)
+                     out, workspace, FORMAT_IF4, amax_in=amax_in)
 
 
 def dequantize(q, inv_rht_signs=None, out_dtype=None, out=None):

@@ -68,6 +68,12 @@ int check_input(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t
     return fail(NVFP4_INVALID_ARG, "scale rules other than MAX6 take NVFP4 with rounding RTN only");
   if (o->rounding == NVFP4_MSEDEN && o->eden_group != 128 && o->eden_group != 16)
     return fail(NVFP4_INVALID_ARG, "eden_group %d is not 128 or 16", o->eden_group);
+  if (o->amax_out && (o->rounding != NVFP4_MSEDEN || o->tensor_scale_in))
+    return fail(NVFP4_UNSUPPORTED, "amax_out is written by MS-EDEN with a computed tensor scale only");
+  if (o->amax_in && (o->rounding == NVFP4_MSEDEN || o->rht || o->tensor_scale_in))
+    return fail(NVFP4_UNSUPPORTED, "amax_in is taken by calls without rotation, MS-EDEN or tensor_scale_in only");
+  if ((o->amax_out && !aligned(o->amax_out, 4)) || (o->amax_in && !aligned(o->amax_in, 4)))
+    return fail(NVFP4_MISALIGNED, "amax_out / amax_in must be 4-byte aligned");
   if (rows < 0 || cols < 0)
     return fail(NVFP4_INVALID_ARG, "negative shape %lld x %lld", (long long)rows, (long long)cols);
   if ((uint64_t)rows > kMaxDim || (uint64_t)cols > kMaxDim)
@@ -144,9 +150,12 @@ void fill_common(QuantParams &p, const void *x, int in_dtype, int64_t rows, int6
   p.ts_out = tensor_scale;
   if (ws) {
     p.partial = static_cast<float *>(ws);
+    p.rpartial = p.partial + kMaxPartials;
     p.tb = reinterpret_cast<float *>(static_cast<char *>(ws) + kPartialBytes);
   }
   p.ts_in = o->tensor_scale_in;
+  p.amax_in = o->amax_in;
+  p.amax_out = o->amax_out;
   for (int i = 0; i < 4; ++i) p.sg[i] = o->rht_signs[i];
   p.rht = o->rht;
   p.group16 = o->eden_group == 16;
@@ -156,7 +165,8 @@ void fill_common(QuantParams &p, const void *x, int in_dtype, int64_t rows, int6
   p.key.stream = o->stream;
 }
 
-// Zero-size tensor: only the tensor scale is defined (the given one, or 1).
+// Zero-size tensor: only the tensor scale is defined (the given one, or 1),
+// and the maximum (0) if it is asked for.
 int write_trivial_scale(const nvfp4_opts *o, float *tensor_scale, hipStream_t s) {
   hipError_t e;
   if (o->tensor_scale_in)
@@ -164,6 +174,10 @@ int write_trivial_scale(const nvfp4_opts *o, float *tensor_scale, hipStream_t s)
   else {
     static const float one = 1.0f;
     e = hipMemcpyAsync(tensor_scale, &one, sizeof(float), hipMemcpyHostToDevice, s);
+  }
+  if (e == hipSuccess && o->amax_out) {
+    static const float zero = 0.0f;
+    e = hipMemcpyAsync(o->amax_out, &zero, sizeof(float), hipMemcpyHostToDevice, s);
   }
   if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "%s", hipGetErrorString(e));
   return ok();
@@ -199,7 +213,7 @@ int quantize_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, int64
                    : o->scale_rule == NVFP4_SCALE_4OVER6 ? kFos
                    : o->scale_rule == NVFP4_SCALE_SEARCH ? kSearch
                                                          : kRtn;
-    if (!o->tensor_scale_in) {
+    if (!o->tensor_scale_in && !o->amax_in) {
       e = launch_quant(p, bf, o->axis, kAmax, grid, s);
       p.npartial = grid;
     }
@@ -216,6 +230,8 @@ int quantize_dual_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, 
   if (!o) return fail(NVFP4_INVALID_ARG, "opts is NULL");
   if (o->rounding != NVFP4_MSEDEN)
     return fail(NVFP4_INVALID_ARG, "the two-axis quantization takes rounding MSEDEN only");
+  if (o->amax_out || o->amax_in)
+    return fail(NVFP4_UNSUPPORTED, "the two-axis quantization takes no amax_out / amax_in");
   nvfp4_opts orow = *o, ocol = *o;
   orow.axis = 0;
   ocol.axis = 1;

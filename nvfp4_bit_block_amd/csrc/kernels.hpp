@@ -27,7 +27,7 @@ constexpr int kMaxPartials = 2048; // workgroups of a pass that writes partials
 // rows (bf16: 2 columns per word, fp32: 1), so a wave tile is 128 rows x
 // 8 * kColWords words of columns.
 constexpr int kColWords = 4;
-constexpr size_t kPartialBytes = 16384;
+constexpr size_t kPartialBytes = 16384;  // partial maxima: two arrays of kMaxPartials floats
 
 struct QuantParams {
   const void *x;
@@ -47,6 +47,9 @@ struct QuantParams {
   uint32_t npartial;    // partial maxima written by the previous pass
   float *tb;            // MS-EDEN target scales, nblocks floats of workspace
   const float *ts_in;   // given tensor scale or nullptr
+  const float *amax_in; // given max|x| (tensor scale amax_in / top) or nullptr
+  float *amax_out;      // MS-EDEN: max|x| of the raw input written here, or nullptr
+  float *rpartial;      // kMaxPartials floats of workspace: partial max|x| for amax_out
   float *rot_out;       // kRot output
   uint32_t sg[4];       // rotation sign words
   int rht;

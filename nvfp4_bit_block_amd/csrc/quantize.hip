@@ -24,6 +24,10 @@ namespace nv4 {
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ float tensor_scale(const QuantParams &p, float *red) {
   if (p.ts_in) return *p.ts_in;
+  if (p.amax_in) {
+    const float a = *p.amax_in;
+    return (a > 0.0f) ? a / p.top : 1.0f;
+  }
   float m = 0.0f;
   for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.partial[i]);
   m = block_max(m, red, kThreads);
@@ -67,6 +71,33 @@ __device__ __forceinline__ void unpack_f32(const uint32_t w[16], const SignMasks
 }
 
 __device__ __forceinline__ uint32_t sign_nib(float z) { return (__float_as_uint(z) >> 28) & 8u; }
+
+// max|x| over N raw input words (bf16 pairs or fp32): for bf16 the largest
+// magnitude bits of the 16-bit halves (integer order is the order of
+// magnitudes), then back to fp32.
+template <int IN_BF16, int N>
+__device__ __forceinline__ float raw_absmax(const uint32_t (&w)[N]) {
+  if constexpr (IN_BF16) {
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    u16x2_t m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < N; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
+    const uint32_t hi = m[0] > m[1] ? m[0] : m[1];
+    return __uint_as_float(hi << 16);
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(__uint_as_float(w[i])));
+    return m;
+  }
+}
+
+// MS-EDEN with amax_out: the workgroup's maximum of |x| (the raw input)
+// goes to the second partial array, which k_eden_scales reduces.
+__device__ __forceinline__ void raw_partial(const QuantParams &p, float araw, float *red) {
+  const float m = block_max(araw, red, kThreads);
+  if (threadIdx.x == 0) p.rpartial[blockIdx.x] = m;
+}
 
 // ---------------------------------------------------------------- outputs
 // Where one block's results go.  PtrSink: plain stores, skipped by lanes
@@ -362,7 +393,8 @@ __device__ __forceinline__ void load_z(const RawBlock<IN_BF16> &b, const SignMas
   }
 }
 
-template <int IN_BF16, int MODE>
+// RAW = 1 (MS-EDEN with amax_out): also the maximum of |x| over the raw input.
+template <int IN_BF16, int MODE, int RAW = 0>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
@@ -376,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   const uint32_t rank = (threadIdx.x & ~63u) + lane_block_rank(threadIdx.x & 63u);
   const SignMasks sm = make_masks<IN_BF16>(p, lig);
   const uint32_t stride = gridDim.x * kThreads;
-  float lmax = 0.0f;
+  float lmax = 0.0f, araw = 0.0f;
   // the next block's loads are issued before the current block is processed
   RawBlock<IN_BF16> cur = {}, nxt = {};
   uint32_t base = blockIdx.x * kThreads;
@@ -389,6 +421,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
     // lanes past the end hold stale values; they fill whole rotation groups
     // and store nothing, so they never reach an output
     float z[16];
+    if constexpr (RAW) {
+      // (lanes past the end hold a copy of the last block: harmless here)
+      uint32_t w[IN_BF16 ? 8 : 16];
+#pragma unroll
+      for (int i = 0; i < (IN_BF16 ? 2 : 4); ++i) {
+        w[4 * i] = cur.q[i].x;
+        w[4 * i + 1] = cur.q[i].y;
+        w[4 * i + 2] = cur.q[i].z;
+        w[4 * i + 3] = cur.q[i].w;
+      }
+      araw = fmaxf(araw, raw_absmax<IN_BF16>(w));
+    }
     load_z<IN_BF16>(cur, sm, p.rht, lig, z);
     if constexpr (MODE == kRot) quant_block<MODE>(z, gb, PtrSink{p, gb, active}, p, s_t, lmax);
     else quant_block<MODE>(z, gb, RowSink(p, base, rank), p, s_t, lmax);
@@ -398,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
     const float m = block_max(lmax, red, kThreads);
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
   }
+  if constexpr (RAW) raw_partial(p, araw, red);
 }
 
 // ---------------------------------------------------------------- axis 1
@@ -471,12 +516,21 @@ __device__ __forceinline__ void col_load(const QuantParams &p, uint32_t tt, uint
 }
 
 // One wave tile (tile row tt, tile column tc).
-template <int IN_BF16, int MODE>
+template <int IN_BF16, int MODE, int RAW = 0>
 __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint32_t tc, uint32_t lig, uint32_t q,
-                                         uint32_t sbits, float s_t, float &lmax) {
+                                         uint32_t sbits, float s_t, float &lmax, float &araw) {
   using C = ColCfg<IN_BF16>;
   ColRaw w;
   col_load<IN_BF16>(p, tt, tc, lig, q, w);
+  if constexpr (RAW) {
+    // the raw tile before any rotation (outside the tensor it holds zeros)
+    uint32_t f[16 * kColWords];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int c = 0; c < kColWords; ++c) f[r * kColWords + c] = w[r][c];
+    araw = fmaxf(araw, raw_absmax<IN_BF16>(f));
+  }
   const uint32_t row0 = tt * 128 + 16 * lig;
   const uint32_t c0 = tc * C::kTileCols + C::kColCols * q;
   const bool rows_ok = row0 < p.rows;
@@ -513,7 +567,8 @@ __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint
   }
 }
 
-template <int IN_BF16, int MODE>
+// RAW as for k_quant_rows.
+template <int IN_BF16, int MODE, int RAW = 0>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
@@ -527,18 +582,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   const uint32_t sbits = p.rht ? lane_sign_bits(p.sg, lig) : 0u;
   const uint32_t nct = p.ctiles_div.d;
   const uint32_t waves = gridDim.x * (kThreads / kWave);
-  float lmax = 0.0f;
+  float lmax = 0.0f, araw = 0.0f;
 
   for (uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6));
        t < p.ntiles; t += waves) {
     const uint32_t tt = fdiv(t, p.ctiles_div);
     const uint32_t tc = t - tt * nct;
-    col_tile<IN_BF16, MODE>(p, tt, tc, lig, q, sbits, s_t, lmax);
+    col_tile<IN_BF16, MODE, RAW>(p, tt, tc, lig, q, sbits, s_t, lmax, araw);
   }
   if constexpr (MODE == kAmax || MODE == kEden) {
     const float m = block_max(lmax, red, kThreads);
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
   }
+  if constexpr (RAW) raw_partial(p, araw, red);
 }
 
 // ---------------------------------------------------------------- both axes
@@ -588,7 +644,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
       quant_block<MODE>(z, active ? gb : 0u, PtrSink{pr, active ? gb : 0u, active}, pr, s_r, lmax_r);
     }
     // column-wise: wave w takes wave tile column 4 * tcw + w
-    col_tile<IN_BF16, MODE>(pc, tt, 4 * tcw + (threadIdx.x >> 6), lig, q, sbits, s_c, lmax_c);
+    float unused = 0.0f;  // (the two-axis call takes no amax_out)
+    col_tile<IN_BF16, MODE>(pc, tt, 4 * tcw + (threadIdx.x >> 6), lig, q, sbits, s_c, lmax_c, unused);
   }
   if constexpr (MODE == kEden) {
     const float mr = block_max(lmax_r, red, kThreads);
@@ -613,6 +670,12 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     s_t = (m > 0.0f) ? m / 448.0f : 1.0f;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  if (p.amax_out && blockIdx.x == 0) {
+    float m = 0.0f;
+    for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.rpartial[i]);
+    m = block_max(m, red, kThreads);
+    if (threadIdx.x == 0) *p.amax_out = m;
+  }
   // Whole calls (8 blocks each): the next call's targets are loaded while
   // this one is coded (clamped to the last call, so the load is unconditional).
   const uint32_t nfull = p.nblocks / 8u;
@@ -681,7 +744,16 @@ static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid
     case kRtn: launch_one<IN_BF16, kRtn>(p, axis, grid, s); break;
     case kSr: launch_one<IN_BF16, kSr>(p, axis, grid, s); break;
     case kIf4: launch_one<IN_BF16, kIf4>(p, axis, grid, s); break;
-    case kEden: launch_one<IN_BF16, kEden>(p, axis, grid, s); break;
+    case kEden:
+      if (p.amax_out) {
+        if (axis == 0)
+          hipLaunchKernelGGL((k_quant_rows<IN_BF16, kEden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
+        else
+          hipLaunchKernelGGL((k_quant_cols<IN_BF16, kEden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
+      } else {
+        launch_one<IN_BF16, kEden>(p, axis, grid, s);
+      }
+      break;
     case kEdenFused: launch_one<IN_BF16, kEdenFused>(p, axis, grid, s); break;
     case kRot: launch_one<IN_BF16, kRot>(p, axis, grid, s); break;
     case kFos: launch_one<IN_BF16, kFos>(p, axis, grid, s); break;

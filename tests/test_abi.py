@@ -41,7 +41,7 @@ def test_header_functions_exported(nv):
 
 def test_version_and_strings(nv):
     L = nv.lib()
-    assert nv.abi_version() == 2
+    assert nv.abi_version() == 3
     for st, text in ((OK, b"ok"), (INVALID, b"invalid argument"), (SHAPE, b"bad shape"),
                      (MISALIGNED, b"misaligned pointer or stride"), (WS_SMALL, b"workspace too small"),
                      (HIP_ERR, b"HIP error"), (UNSUPPORTED, b"unsupported")):
@@ -110,6 +110,20 @@ def test_quantize_rejections(nv):
     assert _q(nv, scale_rule=1, rounding=1) == INVALID        # Four Over Six: RTN only
     assert _q(nv, scale_rule=1, rounding=2) == INVALID
     assert _q(nv, fn="nvfp4_quantize_if4", scale_rule=1) == INVALID
+    # amax_out: MS-EDEN with a computed tensor scale only; amax_in: no
+    # rotation, no given tensor scale, not MS-EDEN; both 4-byte aligned
+    assert _q(nv, rounding=2, amax_out=FAKE, ws_bytes=100) == WS_SMALL   # accepted (fails later)
+    assert _q(nv, rounding=2, axis=1, rows=256, cols=64, amax_out=FAKE, ws_bytes=100) == WS_SMALL
+    assert _q(nv, rounding=0, amax_out=FAKE) == UNSUPPORTED
+    assert _q(nv, rounding=2, amax_out=FAKE, tensor_scale_in=FAKE) == UNSUPPORTED
+    assert _q(nv, rounding=2, amax_out=FAKE + 2) == MISALIGNED
+    assert _q(nv, amax_in=FAKE, ws_bytes=100) == WS_SMALL                 # RTN: accepted
+    assert _q(nv, rounding=1, amax_in=FAKE, ws_bytes=100) == WS_SMALL     # SR
+    assert _q(nv, fn="nvfp4_quantize_if4", amax_in=FAKE, ws_bytes=100) == WS_SMALL
+    assert _q(nv, rounding=2, amax_in=FAKE) == UNSUPPORTED
+    assert _q(nv, rht=1, amax_in=FAKE) == UNSUPPORTED
+    assert _q(nv, amax_in=FAKE, tensor_scale_in=FAKE) == UNSUPPORTED
+    assert _q(nv, amax_in=FAKE + 1) == MISALIGNED
     _q(nv, cols=100)
     assert b"multiple of 16" in L.nvfp4_last_error()
 
@@ -132,6 +146,8 @@ def test_dual_rejections_and_workspace(nv):
     assert d(rows=144) == SHAPE                      # group 128 along the rows
     assert d(rows=144, eden_group=16) == SHAPE       # group 16: still whole 128-row tiles
     assert d(ws_bytes=w0) == WS_SMALL
+    assert d(amax_out=FAKE) == UNSUPPORTED
+    assert d(amax_in=FAKE) == UNSUPPORTED
 
 
 def test_dequantize_and_gemm_rejections(nv):
