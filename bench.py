@@ -406,6 +406,87 @@ def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
             gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
             res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
                          "shape_in": list(x.shape), "what": what}
+    res.update(other_configs(nv, torch))
+    return res
+
+
+def other_configs(nv, torch):
+    """The other workloads of the method's configurations, each on its own
+    seeded inputs (synth.py): the 4096x4096 gradient (rows, rotation, SR and
+    MS-EDEN), the 8192x8192 weight (IF4, RTN) and the weight gradient of a
+    Llama-like linear (dY, X 16384x4096 column-wise with rotation and
+    MS-EDEN, then dW = dY^T X, fp32)."""
+    from nvfp4_bit_block_amd import synth
+    dev = torch.device("cuda:0")
+    res = {}
+
+    def timed(fn, per_graph=20, replays=10):
+        """GPU time per call: these calls are short enough that launching
+        them one by one from Python would leave the GPU waiting for the host,
+        so they are captured in a HIP graph of `per_graph` calls and the
+        graph is replayed (the calls launch kernels only)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (replays * per_graph)
+
+    def q_entry(x, ms, what):
+        gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                "shape_in": list(x.shape), "what": what}
+
+    def buffers(x, rnd, axis):
+        R, K = (x.shape[0], x.shape[1]) if axis == 0 else (x.shape[1], x.shape[0])
+        q = nv.QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                       torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
+                       torch.empty(1, dtype=torch.float32, device=dev))
+        w = torch.empty(nv.workspace_size(x.shape[0], x.shape[1], rnd, axis), dtype=torch.uint8, device=dev)
+        return q, w
+
+    g, gs = synth.gradient(4096, 4096, seed=1)
+    G = torch.from_numpy(g).to(dev).to(torch.bfloat16)
+    for rnd in ("sr", "mseden"):
+        q, w = buffers(G, rnd, 0)
+        ms = timed(lambda: nv.quantize_nvfp4(G, rounding=rnd, rht_signs=gs, seed=1, out=q, workspace=w))
+        res["gradient_4096_" + rnd] = q_entry(G, ms, f"4096x4096 gradient (5 % outliers x10), RHT + {rnd}, rows")
+    del G
+    Wt = torch.from_numpy(synth.weight(8192, 8192, seed=2)).to(dev).to(torch.bfloat16)
+    q, w = buffers(Wt, "rtn", 0)
+    ms = timed(lambda: nv.quantize_if4(Wt, out=q, workspace=w))
+    res["weight_8192_if4"] = q_entry(Wt, ms, "8192x8192 Student-t weight, IF4 RTN, rows")
+    del Wt, q, w
+    dy, x, ws = synth.wgrad(16384, 4096, seed=3)
+    dYw = torch.from_numpy(dy).to(dev).to(torch.bfloat16)
+    Xw = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    qw = {}
+    for name, t in (("wgrad_dY_cols", dYw), ("wgrad_X_cols", Xw)):
+        q, w = qw[name] = buffers(t, "mseden", 1)
+        ms = timed(lambda: nv.quantize_nvfp4(t, rounding="mseden", axis=1, rht_signs=ws, seed=3, out=q,
+                                             workspace=w))
+        res[name] = q_entry(t, ms, "16384x4096, RHT + MS-EDEN along the 16384 rows (weight gradient operand)")
+    qd, qx = qw["wgrad_dY_cols"][0], qw["wgrad_X_cols"][0]
+    dW = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+    ms = timed(lambda: nv.gemm_nvfp4(qd, qx, out=dW))
+    fl = 2.0 * 4096 * 4096 * 16384
+    res["wgrad_gemm_dW"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
+                            "what": "dW = dY^T X [4096 x 4096], K = 16384, fp32 out: 256 tiles, one per CU"}
     return res
 
 
