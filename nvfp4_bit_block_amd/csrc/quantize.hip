@@ -535,6 +535,14 @@ __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint
   const uint32_t c0 = tc * C::kTileCols + C::kColCols * q;
   const bool rows_ok = row0 < p.rows;
   const uint32_t kblk = tt * 8 + lig;
+  // the rotation's sign flips, once per raw word: the sign of a position is
+  // the same for every column (bf16: both halves of a word)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+#pragma unroll
+    for (int c = 0; c < kColWords; ++c) w[r][c] ^= sflip;
+  }
 #pragma unroll
   for (uint32_t j = 0; j < C::kColCols; ++j) {
     const int wi = IN_BF16 ? (int)(j >> 1) : (int)j;
@@ -544,11 +552,8 @@ __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint
     float z[16];
     auto unpack = [&]() {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t sflip = ((sbits >> r) & 1u) ? (IN_BF16 ? 0x80008000u : 0x80000000u) : 0u;
-        const uint32_t v = cw[r] ^ sflip;
-        z[r] = IN_BF16 ? ((j & 1) ? bf16_hi(v) : bf16_lo(v)) : __uint_as_float(v);
-      }
+      for (int r = 0; r < 16; ++r)
+        z[r] = IN_BF16 ? ((j & 1) ? bf16_hi(cw[r]) : bf16_lo(cw[r])) : __uint_as_float(cw[r]);
     };
     unpack();
     // fast stages; the exact ones when the wave holds a zero output (the raw
