@@ -135,6 +135,7 @@ __device__ __forceinline__ half8_t dequant8_lut(uint32_t w, _Float16 s, uint32_t
 
 // LDS stage: [buffer][fragment 0..15 (A 0..7, B 8..15)][step][lane] x 16 bytes.
 typedef half8_t Stage[2][16][kSteps][64];
+static_assert(sizeof(Stage) == 16 * 8192, "the epilogue gives each of the 16 waves 8 KB of the stage");
 
 // The two fp16 block scales of this lane half (bytes 2h, 2h+1 of the word)
 // and, for IF4 operands, their INT flags (bits 7 and 15 of f).
@@ -181,12 +182,15 @@ __device__ __forceinline__ void read_ops(Ops &op, const Stage &st, int b, uint32
   for (int m = 0; m < 2; ++m) op.a[m] = st[b][2 * wm + m][j][lane];
 }
 
+// B is the first MFMA operand: the 32 x 32 result is the transposed tile,
+// so that a lane holds one output row and, for each group of four
+// accumulators, four adjacent output columns (see the epilogue).
 __device__ __forceinline__ void mfma16(const Ops &op, float16_t (&acc)[2][2]) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n)
-      acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op.a[m], op.b[n], acc[m][n], 0, 0, 0);
+      acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op.b[n], op.a[m], acc[m][n], 0, 0, 0);
 }
 
 // Interleave one step: each MFMA followed by up to NV vector-ALU instructions
@@ -348,26 +352,87 @@ __global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: D layout of a 32x32 tile -- lane holds column (lane % 32)
-  // and rows 8*(e/4) + 4*h + (e%4), e = 0..15.
+  // ---- epilogue.  With B as the first MFMA operand, lane (r32, h) of tile
+  // (m, n) holds output row 32m + r32 of the wave tile and, in accumulators
+  // 4q .. 4q+3, its columns 32n + 8q + 4h .. +3.  The wave scales and
+  // rounds them, writes its tile to its own 8 KB of the (now idle) stage,
+  // and reads it back by rows, so that every lane stores 16 contiguous
+  // bytes and eight (bf16) or sixteen (fp32) lanes cover a whole row of the
+  // wave tile.  The 16-byte column chunks of a row are XOR-swizzled by the
+  // row so that both the writes and the reads spread over all LDS banks.
   const float alpha = (*p.a_ts) * (*p.b_ts);
+  uint8_t *const wbuf = reinterpret_cast<uint8_t *>(&st) + w * 8192u;
+  const uint32_t row0 = m0 + wm * 64, col0 = n0 + wn * kWaveCols;
+  const uint32_t esz = OUT_BF16 ? 2 : 4;
+  // 16-byte stores need a 16-byte aligned row start in every row
+  const bool vec = ((reinterpret_cast<uintptr_t>(p.c) | (uintptr_t)(p.ldc * esz)) & 15u) == 0;
+  if (OUT_BF16) {
+    // the whole 64 x 64 wave tile, rows of 128 bytes (8 chunks)
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t rl = 32 * m + r32;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const uint32_t col = n0 + wn * kWaveCols + 32 * n + r32;
-      if (col >= p.N) continue;
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t row = m0 + wm * 64 + 32 * m + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (row >= p.M) continue;
-        const float v = acc[m][n][e] * alpha;
-        if (OUT_BF16) {
-          const uint32_t u = __float_as_uint(v);
-          static_cast<uint16_t *>(p.c)[(size_t)row * p.ldc + col] =
-              (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        for (int q = 0; q < 4; ++q) {
+          uint32_t b[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t u = __float_as_uint(acc[m][n][4 * q + t] * alpha);
+            b[t] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // bf16, nearest even
+          }
+          const uint32_t chunk = (4 * n + q) ^ ((rl >> 1) & 7u);
+          *reinterpret_cast<uint2 *>(wbuf + rl * 128 + chunk * 16 + 8 * h) =
+              uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t rl = 8 * i + (lane >> 3), cc = lane & 7u;
+      const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + rl * 128 + ((cc ^ ((rl >> 1) & 7u)) * 16));
+      const uint32_t row = row0 + rl, col = col0 + 8 * cc;
+      if (row >= p.M || col >= p.N) continue;
+      uint16_t *dst = static_cast<uint16_t *>(p.c) + (size_t)row * p.ldc + col;
+      if (vec && col + 8 <= p.N) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (col + t < p.N) dst[t] = (uint16_t)(vv[t >> 1] >> (16 * (t & 1)));
+      }
+    }
+  } else {
+    // fp32: one 32 x 64 half (m) of the wave tile at a time, rows of 256
+    // bytes (16 chunks)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (m) __syncthreads();  // the reads of the first half are done
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t chunk = (8 * n + 2 * q + h) ^ (r32 & 15u);
+          *reinterpret_cast<float4 *>(wbuf + r32 * 256 + chunk * 16) =
+              float4{acc[m][n][4 * q] * alpha, acc[m][n][4 * q + 1] * alpha, acc[m][n][4 * q + 2] * alpha,
+                     acc[m][n][4 * q + 3] * alpha};
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t rl = 4 * i + (lane >> 4), cc = lane & 15u;
+        const float4 v = *reinterpret_cast<const float4 *>(wbuf + rl * 256 + ((cc ^ (rl & 15u)) * 16));
+        const uint32_t row = row0 + 32 * m + rl, col = col0 + 4 * cc;
+        if (row >= p.M || col >= p.N) continue;
+        float *dst = static_cast<float *>(p.c) + (size_t)row * p.ldc + col;
+        if (vec && col + 4 <= p.N) {
+          *reinterpret_cast<float4 *>(dst) = v;
         } else {
-          static_cast<float *>(p.c)[(size_t)row * p.ldc + col] = v;
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (col + t < p.N) dst[t] = vv[t];
         }
       }
     }

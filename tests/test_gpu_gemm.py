@@ -63,6 +63,29 @@ def test_gemm_ldc_and_strided_output(nv):
     assert np.all(h[:, :10] == -7.0) and np.all(h[:, 80:] == -7.0)
 
 
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("M,N,ldc", [(300, 259, 264), (70, 202, 208), (257, 520, 520)])
+def test_gemm_output_rows_with_aligned_stride(nv, dtype, M, N, ldc):
+    """Output rows whose starts are 16-byte aligned (full-width stores) with a
+    ragged last column group and ragged rows: every element of [M x N] is
+    written once and the columns N .. ldc-1 of each row stay untouched."""
+    import torch
+    rng = np.random.default_rng(M + N + ldc)
+    K = 320
+    a = oracle.quantize(rng.standard_normal((M, K)).astype(np.float32))
+    b = oracle.quantize(rng.standard_normal((N, K)).astype(np.float32))
+    ref = oracle.gemm_full(a, b)
+    td = getattr(torch, dtype)
+    big = torch.full((M, ldc), -7.0, dtype=td, device="cuda:0")
+    nv.gemm_nvfp4(upload(nv, a), upload(nv, b), out=big[:, :N])
+    h = big.float().cpu().numpy()
+    if dtype == "float32":
+        assert rel_fro(h[:, :N], ref) <= 1e-5
+    else:
+        assert np.all(np.abs(h[:, :N] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+    assert np.all(h[:, N:] == -7.0)
+
+
 def test_gemm_rotated_operands_match_unrotated_product(nv):
     """With the same signs on both operands, (H D a) . (H D b) = a . b: the
     GEMM of rotated, MS-EDEN-quantized operands estimates A B^T."""
