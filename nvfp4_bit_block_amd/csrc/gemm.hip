@@ -16,7 +16,7 @@
 // Tiling: a workgroup of 16 waves (four per SIMD, so that others can issue
 // while one waits on LDS or the barrier) computes a 256 x 256 tile; wave
 // (wm, wn) a 64 x 64 sub-tile as 2 x 2 MFMA tiles of 32 x 32 (64 fp32
-// accumulators per lane, 118 VGPRs in all).  K advances in chunks of 64
+// accumulators per lane, about 125 VGPRs in all).  K advances in chunks of 64
 // (four 16-wide MFMA steps).  The tile's 16 row fragments per chunk (8 of A,
 // 8 of B, 32 rows each) are split between the waves: wave w loads fragment w
 // (A for w < 8, B after; buffer loads, rows past M or N read as zero),
@@ -35,10 +35,16 @@
 // k0 + 32h .. k0 + 32h + 31 and feeds dword j of them to step j.  A and B use
 // the same assignment, so the permutation of k cancels.
 //
-// Workgroup order: workgroups are dispatched round-robin to the 8 XCDs; the
-// logical tile index is remapped so that each XCD receives a contiguous run,
-// and runs are laid out in groups of 4 tile-rows so that the 32 workgroups
-// resident on one XCD share A and B panels in that XCD's L2.
+// Workgroup order: the grid holds one workgroup per compute unit (a
+// multiple of 8), each looping over tiles bid, bid + grid, ...; workgroups
+// are dispatched round-robin to the 8 XCDs, so a workgroup's tiles all
+// belong to its XCD.  The tile index is remapped so that each XCD receives
+// a contiguous run, laid out in groups of 4 tile-rows so that the 32
+// workgroups resident on one XCD share A and B panels in that XCD's L2.
+//
+// Epilogue: the accumulators go through LDS (each wave's 64 x 64 tile in
+// its own 8 KB of the stage) so that the output is written in 16-byte row
+// segments; the next tile's first operand loads are issued before it.
 #include "kernels.hpp"
 
 namespace nv4 {
@@ -248,119 +254,26 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OUT_BF16, int FAST, int IF4>
-__global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
-  __shared__ Stage st;
-  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t r32 = lane & 31u, h = lane >> 5;
-
-  // ---- tile of this workgroup
-  const uint32_t tiles_m = (p.M + kTile - 1) / kTile, tiles_n = (p.N + kTile - 1) / kTile;
-  const uint32_t nt = tiles_m * tiles_n;
-  const uint32_t bid = blockIdx.x;
-  const uint32_t per = nt / kXcds, rem = nt % kXcds, xcd = bid % kXcds, idx = bid / kXcds;
-  const uint32_t lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const uint32_t group = lid / (kGroupM * tiles_n);
-  const uint32_t first_m = group * kGroupM;
-  const uint32_t gsz = min(tiles_m - first_m, kGroupM);
-  const uint32_t in_group = lid - group * kGroupM * tiles_n;
-  const uint32_t tm = first_m + in_group % gsz, tn = in_group / gsz;
-
-  const uint32_t K = p.K, K2 = K / 2, K16 = K / 16;
-  const uint32_t m0 = tm * kTile, n0 = tn * kTile;
-  const uint32_t rows_a = min(kTile, p.M - m0), rows_b = min(kTile, p.N - n0);
-  const uint32_t wm = w >> 2, wn = w & 3u;   // wave tile: rows 64 wm.., columns 64 wn..
-
-  Panels P;
-  if (w < 8) {
-    P.c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_codes + (size_t)m0 * K2), (short)0,
-                                            (int)(rows_a * K2), kRsrcWord3);
-    P.s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_scales + (size_t)m0 * K16), (short)0,
-                                            (int)(rows_a * K16), kRsrcWord3);
-  } else {
-    P.c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_codes + (size_t)n0 * K2), (short)0,
-                                            (int)(rows_b * K2), kRsrcWord3);
-    P.s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_scales + (size_t)n0 * K16), (short)0,
-                                            (int)(rows_b * K16), kRsrcWord3);
-  }
-  {
-    const uint32_t row = 32 * (w & 7u) + r32;  // this lane's row of its fragment
-    P.vo_c = row * K2 + 16 * h;
-    P.vo_s = row * K16;
-  }
-  P.K = K;
-  P.h = h;
-
-  float16_t acc[2][2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.0f;
-
-  const uint32_t nfull = FAST ? K / kChunk : 0;
-  if (nfull > 0) {
-    // Prologue: chunk 0 into buffer 0; chunk 1 in r1 and chunk 2 in r0
-    // (loads of chunks past the end re-read the last chunk, unused).
-    const uint32_t klast = (nfull - 1) * kChunk;
-    Raw r0, r1;
-    // (sched barriers keep the loads in this order, which the wait counts
-    // of the steady-state loop assume)
-    load_fast(r0, P, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_fast(r1, P, min(kChunk, klast));
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      Scales<IF4> s;
-      scales16<IF4>(r0, P.h, s);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dequant_item<IF4>(st, 0, r0, s, w, lane, j);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    load_fast(r0, P, min(2 * kChunk, klast));
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    Ops op;
-    read_ops(op, st, 0, wm, wn, lane, 0);
-    // Steady state: chunk c+1's codes are in r1 (c even) or r0 (c odd).
-    // The chunk after the last dequantizes stale codes into the idle buffer.
-    uint32_t c = 0;
-    for (; c + 1 < nfull; c += 2) {
-      chunk<IF4>(st, c, min((c + 3) * kChunk, klast), r1, op, P, w, wm, wn, lane, acc);
-      chunk<IF4>(st, c + 1, min((c + 4) * kChunk, klast), r0, op, P, w, wm, wn, lane, acc);
-    }
-    if (c < nfull) chunk<IF4>(st, c, klast, r1, op, P, w, wm, wn, lane, acc);
-    __syncthreads();  // every wave is done with both buffers before any reuse below
-  }
-  // remaining K (K % 64 != 0): one chunk at a time through buffer 0
-  for (uint32_t k0 = nfull * kChunk; k0 < K; k0 += kChunk) {
-    Raw r;
-    load_generic(r, P, k0);
-    Scales<IF4> s;
-    scales16<IF4>(r, P.h, s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dequant_item<IF4>(st, 0, r, s, w, lane, j);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < (int)kSteps; ++j) {
-      Ops op;
-      read_ops(op, st, 0, wm, wn, lane, j);
-      mfma16(op, acc);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue.  With B as the first MFMA operand, lane (r32, h) of tile
-  // (m, n) holds output row 32m + r32 of the wave tile and, in accumulators
-  // 4q .. 4q+3, its columns 32n + 8q + 4h .. +3.  The wave scales and
-  // rounds them, writes its tile to its own 8 KB of the (now idle) stage,
-  // and reads it back by rows, so that every lane stores 16 contiguous
-  // bytes and eight (bf16) or sixteen (fp32) lanes cover a whole row of the
-  // wave tile.  The 16-byte column chunks of a row are XOR-swizzled by the
-  // row so that both the writes and the reads spread over all LDS banks.
+// Epilogue.  With B as the first MFMA operand, lane (r32, h) of tile
+// (m, n) holds output row 32m + r32 of the wave tile and, in accumulators
+// 4q .. 4q+3, its columns 32n + 8q + 4h .. +3.  The wave scales and
+// rounds them, writes its tile to its own 8 KB of the (now idle) stage,
+// and reads it back by rows, so that every lane stores 16 contiguous
+// bytes and eight (bf16) or sixteen (fp32) lanes cover a whole row of the
+// wave tile.  The 16-byte column chunks of a row are XOR-swizzled by the
+// row so that both the writes and the reads spread over all LDS banks.
+template <int OUT_BF16>
+__device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][2], const GemmParams &p, uint32_t m0,
+                                           uint32_t n0, uint32_t w) {
+  const uint32_t wm = w >> 2, wn = w & 3u;
   const float alpha = (*p.a_ts) * (*p.b_ts);
+  // (the lane index is re-derived opaquely, so that the compiler does not
+  // hoist the epilogue's addresses out of the tile loop and keep them live
+  // through the main loop)
+  uint32_t lane = threadIdx.x;
+  asm volatile("" : "+v"(lane));
+  lane &= 63u;
+  const uint32_t r32 = lane & 31u, h = lane >> 5;
   uint8_t *const wbuf = reinterpret_cast<uint8_t *>(&st) + w * 8192u;
   const uint32_t row0 = m0 + wm * 64, col0 = n0 + wn * kWaveCols;
   const uint32_t esz = OUT_BF16 ? 2 : 4;
@@ -439,22 +352,173 @@ __global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
   }
 }
 
-template <int IF4>
-static void launch_fmt(const GemmParams &p, int out_bf16, uint32_t tiles, hipStream_t s) {
-  const bool fast = (p.K % 64) == 0;
-  if (out_bf16) {
-    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(tiles), dim3(1024), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(tiles), dim3(1024), 0, s, p);
+// Placement of workgroup-order tile `bid`: workgroups are dispatched
+// round-robin to the XCDs, so tile bid is remapped such that each XCD
+// receives a contiguous run, laid out in groups of kGroupM tile-rows.
+__device__ __forceinline__ void tile_at(uint32_t bid, uint32_t tiles_m, uint32_t tiles_n, uint32_t &m0, uint32_t &n0) {
+  const uint32_t nt = tiles_m * tiles_n;
+  const uint32_t per = nt / kXcds, rem = nt % kXcds, xcd = bid % kXcds, idx = bid / kXcds;
+  const uint32_t lid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const uint32_t group = lid / (kGroupM * tiles_n);
+  const uint32_t first_m = group * kGroupM;
+  const uint32_t gsz = min(tiles_m - first_m, kGroupM);
+  const uint32_t in_group = lid - group * kGroupM * tiles_n;
+  m0 = (first_m + in_group % gsz) * kTile;
+  n0 = (in_group / gsz) * kTile;
+}
+
+// Wave w's operand panel (A rows m0.., or B rows n0..) of a tile.
+__device__ __forceinline__ void make_panels(Panels &P, const GemmParams &p, uint32_t m0, uint32_t n0, uint32_t w,
+                                            uint32_t r32, uint32_t h) {
+  const uint32_t K2 = p.K / 2, K16 = p.K / 16;
+  if (w < 8) {
+    const uint32_t rows = min(kTile, p.M - m0);
+    P.c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_codes + (size_t)m0 * K2), (short)0, (int)(rows * K2),
+                                            kRsrcWord3);
+    P.s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.a_scales + (size_t)m0 * K16), (short)0, (int)(rows * K16),
+                                            kRsrcWord3);
   } else {
-    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(tiles), dim3(1024), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(tiles), dim3(1024), 0, s, p);
+    const uint32_t rows = min(kTile, p.N - n0);
+    P.c = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_codes + (size_t)n0 * K2), (short)0, (int)(rows * K2),
+                                            kRsrcWord3);
+    P.s = __builtin_amdgcn_make_buffer_rsrc((void *)(p.b_scales + (size_t)n0 * K16), (short)0, (int)(rows * K16),
+                                            kRsrcWord3);
+  }
+  const uint32_t row = 32 * (w & 7u) + r32;  // this lane's row of its fragment
+  P.vo_c = row * K2 + 16 * h;
+  P.vo_s = row * K16;
+  P.K = p.K;
+  P.h = h;
+}
+
+template <int OUT_BF16, int FAST, int IF4>
+__global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
+  __shared__ Stage st;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t r32 = lane & 31u, h = lane >> 5;
+  const uint32_t wm = w >> 2, wn = w & 3u;  // wave tile: rows 64 wm.., columns 64 wn..
+
+  // Tiles of this workgroup: bid, bid + gridDim.x, ...  The grid is a
+  // multiple of the XCD count (or covers every tile at once), so all of a
+  // workgroup's tiles map to the XCD it runs on.  The next tile's first two
+  // chunks are loaded before this tile's epilogue, so that their latency
+  // overlaps the output stores.
+  const uint32_t tiles_m = (p.M + kTile - 1) / kTile, tiles_n = (p.N + kTile - 1) / kTile;
+  const uint32_t nt = tiles_m * tiles_n;
+  const uint32_t K = p.K;
+  const uint32_t nfull = FAST ? K / kChunk : 0;
+  const uint32_t klast = nfull > 0 ? (nfull - 1) * kChunk : 0;
+  uint32_t bid = blockIdx.x, m0, n0;
+  tile_at(bid, tiles_m, tiles_n, m0, n0);
+  Panels P;
+  make_panels(P, p, m0, n0, w, r32, h);
+  // chunk 0 in r0, chunk 1 in r1 (loads of chunks past the end re-read the
+  // last chunk, unused); sched barriers keep the loads in this order
+  Raw r0, r1;
+  if (nfull > 0) {
+    load_fast(r0, P, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_fast(r1, P, min(kChunk, klast));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (;;) {
+    float16_t acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.0f;
+
+    if (nfull > 0) {
+      // Prologue: chunk 0 into buffer 0, then chunk 2 into r0.
+      {
+        Scales<IF4> s;
+        scales16<IF4>(r0, P.h, s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dequant_item<IF4>(st, 0, r0, s, w, lane, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_fast(r0, P, min(2 * kChunk, klast));
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      Ops op;
+      read_ops(op, st, 0, wm, wn, lane, 0);
+      // Steady state: chunk c+1's codes are in r1 (c even) or r0 (c odd).
+      // The chunk after the last dequantizes stale codes into the idle buffer.
+      uint32_t c = 0;
+      for (; c + 1 < nfull; c += 2) {
+        chunk<IF4>(st, c, min((c + 3) * kChunk, klast), r1, op, P, w, wm, wn, lane, acc);
+        chunk<IF4>(st, c + 1, min((c + 4) * kChunk, klast), r0, op, P, w, wm, wn, lane, acc);
+      }
+      if (c < nfull) chunk<IF4>(st, c, klast, r1, op, P, w, wm, wn, lane, acc);
+      __syncthreads();  // every wave is done with both buffers before any reuse below
+    }
+    // remaining K (K % 64 != 0): one chunk at a time through buffer 0
+    for (uint32_t k0 = nfull * kChunk; k0 < K; k0 += kChunk) {
+      Raw r;
+      load_generic(r, P, k0);
+      Scales<IF4> s;
+      scales16<IF4>(r, P.h, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dequant_item<IF4>(st, 0, r, s, w, lane, j);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < (int)kSteps; ++j) {
+        Ops op;
+        read_ops(op, st, 0, wm, wn, lane, j);
+        mfma16(op, acc);
+      }
+      __syncthreads();
+    }
+
+    const uint32_t nbid = bid + gridDim.x;
+    const uint32_t cm0 = m0, cn0 = n0;
+    if (nbid < nt) {
+      tile_at(nbid, tiles_m, tiles_n, m0, n0);
+      make_panels(P, p, m0, n0, w, r32, h);
+      if (nfull > 0) {
+        load_fast(r0, P, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_fast(r1, P, min(kChunk, klast));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    store_tile<OUT_BF16>(st, acc, p, cm0, cn0, w);
+    if (nbid >= nt) break;
+    __syncthreads();  // every wave has read its output back before the next tile's stage writes
+    bid = nbid;
   }
 }
 
+template <int IF4>
+static void launch_fmt(const GemmParams &p, int out_bf16, uint32_t grid, hipStream_t s) {
+  const bool fast = (p.K % 64) == 0;
+  if (out_bf16) {
+    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(grid), dim3(1024), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(grid), dim3(1024), 0, s, p);
+  } else {
+    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(grid), dim3(1024), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(grid), dim3(1024), 0, s, p);
+  }
+}
+
+// One workgroup per compute unit (the stage takes most of a CU's LDS), a
+// multiple of the XCD count; fewer when there are fewer tiles.
+static uint32_t gemm_grid(uint32_t tiles) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return tiles;
+  const uint32_t g = ((uint32_t)(cus > 0 ? cus : 0) / kXcds) * kXcds;
+  return (g == 0 || tiles <= g) ? tiles : g;
+}
+
 hipError_t launch_gemm(const GemmParams &p, int out_bf16, int if4, hipStream_t s) {
-  const uint32_t tiles = ((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile);
-  if (if4) launch_fmt<1>(p, out_bf16, tiles, s);
-  else launch_fmt<0>(p, out_bf16, tiles, s);
+  const uint32_t grid = gemm_grid(((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile));
+  if (if4) launch_fmt<1>(p, out_bf16, grid, s);
+  else launch_fmt<0>(p, out_bf16, grid, s);
   return hipGetLastError();
 }
 

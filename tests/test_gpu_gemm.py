@@ -86,6 +86,32 @@ def test_gemm_output_rows_with_aligned_stride(nv, dtype, M, N, ldc):
     assert np.all(h[:, N:] == -7.0)
 
 
+def test_gemm_more_tiles_than_workgroups(nv):
+    """17 x 18 = 306 output tiles of 256 x 256, more than one per compute
+    unit, so workgroups take several tiles each; ragged in M and N.  Checked
+    on the first, last and one random row and column of every tile (every
+    tile's corners and the ragged edges), in fp32 and bf16."""
+    import torch
+    rng = np.random.default_rng(306)
+    M, N, K = 4100, 4500, 64
+    a = oracle.quantize(rng.standard_normal((M, K)).astype(np.float32))
+    b = oracle.quantize(rng.standard_normal((N, K)).astype(np.float32))
+
+    def picks(n):
+        out = []
+        for t0 in range(0, n, 256):
+            t1 = min(t0 + 256, n)
+            out += [t0, int(rng.integers(t0, t1)), t1 - 1]
+        return np.array(out)
+    rows, cols = picks(M), picks(N)
+    im, in_ = np.repeat(rows, cols.size), np.tile(cols, rows.size)
+    ref = oracle.gemm_entries(a, b, im, in_)
+    c = nv.gemm_nvfp4(upload(nv, a), upload(nv, b)).cpu().numpy()[im, in_]
+    assert rel_fro(c, ref) <= 1e-5
+    c16 = nv.gemm_nvfp4(upload(nv, a), upload(nv, b), out_dtype=torch.bfloat16).float().cpu().numpy()[im, in_]
+    assert np.all(np.abs(c16 - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
 def test_gemm_rotated_operands_match_unrotated_product(nv):
     """With the same signs on both operands, (H D a) . (H D b) = a . b: the
     GEMM of rotated, MS-EDEN-quantized operands estimates A B^T."""
