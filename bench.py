@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extra configurations after the step (profiling runs: then every "
+                         "k_gemm launch is one of the step's GEMMs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -344,7 +347,8 @@ def main():
         "kernels": kernels,
     }
 
-    result["extras"] = extras(nv, torch, stream, X, W, dY, signs, outs, wss, args.steps)
+    if not args.no_extras:
+        result["extras"] = extras(nv, torch, stream, X, W, dY, signs, outs, wss, args.steps)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(Xh, Wh, dYh, signs, args.cpu_seconds)
