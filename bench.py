@@ -387,6 +387,22 @@ def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
                            "what": "RHT + MS-EDEN of dY along rows and columns from one read "
                                    "(input once, two sets of codes and scales)"}
     del wsd
+    # the Y GEMM with its output coded as NVFP4 in the same kernel (RTN along
+    # N, the tensor scale from a first call's max |Y|), on the step's operands
+    Mq, Nq = X.shape[0], W.shape[0]
+    ymax = torch.zeros(1, dtype=torch.float32, device=X.device)
+    qy = nv.QTensor(torch.empty((Mq, Nq // 2), dtype=torch.uint8, device=X.device),
+                    torch.empty((Mq, Nq // 16), dtype=torch.uint8, device=X.device),
+                    torch.ones(1, dtype=torch.float32, device=X.device), nv.FORMAT_NVFP4)
+    nv.gemm_nvfp4_rtn(outs["qX"], outs["qW"], qy.tensor_scale, amax_out=ymax, out=qy)
+    qy.tensor_scale.copy_(ymax / 2688.0)
+    ms = timed(lambda: nv.gemm_nvfp4_rtn(outs["qX"], outs["qW"], qy.tensor_scale, amax_out=ymax, out=qy))
+    fl = 2.0 * Mq * Nq * X.shape[1]
+    res["gemm_Y_nvfp4_out"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                               "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
+                               "what": "Y = X W^T written as NVFP4 (RTN along N with a given tensor scale, "
+                                       "max |Y| out) by the GEMM itself instead of bf16"}
+    del qy
     # IF4 forward operands (the output buffers of the step are reused), then
     # the Y GEMM on them through the INT-flag-aware entry point
     qa = nv.quantize_if4(X, out=outs["qX"], workspace=wss["qX"])

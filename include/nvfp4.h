@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -268,6 +268,32 @@ int nvfp4_gemm_if4(const uint8_t *a_codes, const uint8_t *a_scales, const float 
                    const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
                    int64_t M, int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc,
                    void *stream);
+
+/*
+ * The NVFP4 GEMM with its output coded as NVFP4 in the same kernel [QII-sum
+ * "Quantisierung im Vorwaertsdurchlauf" (RTN, one E4M3 scale per 16
+ * elements, one fp32 scale per tensor); QII-abs (every linear-layer operand
+ * in NVFP4)]: C = (ts_a * ts_b) * A_hat @ B_hat^T as in nvfp4_gemm_nvfp4,
+ * then each row of C coded along N exactly as nvfp4_quantize_nvfp4 codes an
+ * fp32 input with rounding RTN, axis 0, no rotation and tensor_scale_in =
+ * c_ts: scale byte e = E4M3_RNE((max|block| / 6) / s_t), codes of
+ * c / (E4M3(e) * s_t) on the E2M1 grid, round to nearest even.  The result
+ * is the next layer's NVFP4 input without writing or re-reading C.
+ * c_ts: DEVICE fp32, the tensor scale to code with (max |C| is not known
+ * before C is computed, so it comes from the caller, e.g. from c_amax of an
+ * earlier step divided by 6 * 448).  c_codes: DEVICE [M x N/2] bytes,
+ * c_scales: DEVICE [M x N/16] bytes, both 16-byte aligned, as the
+ * quantizer's output for rows_out = M, K = N.  c_amax: DEVICE fp32 or NULL;
+ * receives max |C| over all entries (cleared by the call itself).
+ * Operands: NVFP4 only (IF4 blocks are read as E4M3 scales).  N % 16 == 0
+ * (else NVFP4_BAD_SHAPE); other shapes, limits and errors as
+ * nvfp4_gemm_nvfp4.  Codes can differ from coding the fp64 product where an
+ * fp32 entry lies within accumulation error of a rounding boundary.
+ */
+int nvfp4_gemm_nvfp4_rtn(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                         const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+                         int64_t M, int64_t N, int64_t K, const float *c_ts, uint8_t *c_codes,
+                         uint8_t *c_scales, float *c_amax, void *stream);
 
 /*
  * The rotation alone, for checking it: out[rows_out x K] fp32 = the rotated

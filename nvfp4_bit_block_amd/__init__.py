@@ -18,7 +18,7 @@ __all__ = [
     "RTN", "SR", "MSEDEN", "FORMAT_NVFP4", "FORMAT_IF4", "QTensor", "NvFp4Error",
     "lib", "signs_to_words", "workspace_size", "quantize_nvfp4", "quantize_if4",
     "dequantize", "gemm_nvfp4", "rht", "abi_version", "SCALE_MAX6", "SCALE_4OVER6", "SCALE_SEARCH",
-    "quantize_nvfp4_dual", "workspace_size_dual",
+    "quantize_nvfp4_dual", "workspace_size_dual", "gemm_nvfp4_rtn",
 ]
 
 RTN, SR, MSEDEN = 0, 1, 2
@@ -86,6 +86,8 @@ def lib():
     for name in ("nvfp4_gemm_nvfp4", "nvfp4_gemm_if4"):
         getattr(L, name).restype = INT
         getattr(L, name).argtypes = [P, P, P, P, P, P, I64, I64, I64, P, INT, I64, P]
+    L.nvfp4_gemm_nvfp4_rtn.restype = INT
+    L.nvfp4_gemm_nvfp4_rtn.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P, P, P]
     L.nvfp4_rht.restype = INT
     L.nvfp4_rht.argtypes = [P, INT, I64, I64, I64, INT, P, P, P]
     L.nvfp4_status_string.restype = ctypes.c_char_p
@@ -320,6 +322,36 @@ def gemm_nvfp4(a, b, out_dtype=None, out=None):
                                 ctypes.c_void_p(b.tensor_scale.data_ptr()), M, N, a.k,
                                 ctypes.c_void_p(out.data_ptr()), _dtype_code(out, torch), ldc,
                                 _stream(torch))
+    _check(rc)
+    return out
+
+
+def gemm_nvfp4_rtn(a, b, tensor_scale, amax_out=None, out=None):
+    """The NVFP4 GEMM with its output [M, N] coded as NVFP4 (RTN along N,
+    tensor scale `tensor_scale`, a float32 device tensor [1]) in the same
+    kernel.  Returns a QTensor (rows M, K = N) that holds `tensor_scale`;
+    amax_out (float32 device [1]) receives max |C|.  `out` may give a
+    preallocated QTensor."""
+    import torch
+    if a.k != b.k:
+        raise NvFp4Error(f"K mismatch: {a.k} vs {b.k}")
+    if a.format != FORMAT_NVFP4 or b.format != FORMAT_NVFP4:
+        raise NvFp4Error("operands must be NVFP4 QTensors")
+    for t in (tensor_scale, amax_out):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or t.numel() < 1):
+            raise NvFp4Error("tensor_scale and amax_out must be float32 device tensors")
+    M, N = a.rows, b.rows
+    if out is None:
+        dev = a.codes.device
+        out = QTensor(torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+                      torch.empty((M, N // 16), dtype=torch.uint8, device=dev), tensor_scale, FORMAT_NVFP4)
+    rc = lib().nvfp4_gemm_nvfp4_rtn(
+        ctypes.c_void_p(a.codes.data_ptr()), ctypes.c_void_p(a.scales.data_ptr()),
+        ctypes.c_void_p(a.tensor_scale.data_ptr()), ctypes.c_void_p(b.codes.data_ptr()),
+        ctypes.c_void_p(b.scales.data_ptr()), ctypes.c_void_p(b.tensor_scale.data_ptr()), M, N, a.k,
+        ctypes.c_void_p(tensor_scale.data_ptr()), ctypes.c_void_p(out.codes.data_ptr()),
+        ctypes.c_void_p(out.scales.data_ptr()),
+        None if amax_out is None else ctypes.c_void_p(amax_out.data_ptr()), _stream(torch))
     _check(rc)
     return out
 

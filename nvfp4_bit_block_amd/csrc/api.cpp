@@ -361,11 +361,11 @@ int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *t
 }
 
 namespace {
-int gemm_impl(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
-              const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts, int64_t M,
-              int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc, void *stream, int if4) {
-  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16)
-    return fail(NVFP4_INVALID_ARG, "out_dtype %d is not NVFP4_F32 or NVFP4_BF16", out_dtype);
+// Shape and operand checks shared by the GEMM entry points; fills the
+// operand fields of p.  Returns NVFP4_OK or the failure's status.
+int gemm_operands(GemmParams &p, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                  const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts, int64_t M, int64_t N,
+                  int64_t K) {
   if (M < 0 || N < 0 || K < 0) return fail(NVFP4_INVALID_ARG, "negative shape");
   if ((uint64_t)M > kMaxDim || (uint64_t)N > kMaxDim || (uint64_t)K > kMaxDim)
     return fail(NVFP4_UNSUPPORTED, "dimension above 2^31 - 1");
@@ -374,28 +374,42 @@ int gemm_impl(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts
   // buffer resource with a 32-bit byte range
   if ((uint64_t)K * 128u > 0x7FFFFFFFull)
     return fail(NVFP4_UNSUPPORTED, "K %lld above 16777200", (long long)K);
-  if (ldc < N) return fail(NVFP4_BAD_SHAPE, "ldc %lld < N %lld", (long long)ldc, (long long)N);
+  p = GemmParams{};
+  p.M = (uint32_t)M;
+  p.N = (uint32_t)N;
+  p.K = (uint32_t)K;
   if (M == 0 || N == 0) return ok();
-  if (!a_codes || !a_scales || !a_ts || !b_codes || !b_scales || !b_ts || !c)
+  if (!a_codes || !a_scales || !a_ts || !b_codes || !b_scales || !b_ts)
     return fail(NVFP4_INVALID_ARG, "null device pointer");
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 16) ||
       !aligned(b_scales, 16))
     return fail(NVFP4_MISALIGNED, "codes and scales must be 16-byte aligned");
-  if (!aligned(c, out_dtype == NVFP4_BF16 ? 2 : 4) || !aligned(a_ts, 4) || !aligned(b_ts, 4))
-    return fail(NVFP4_MISALIGNED, "c or a tensor scale is misaligned");
-  GemmParams p;
+  if (!aligned(a_ts, 4) || !aligned(b_ts, 4)) return fail(NVFP4_MISALIGNED, "a tensor scale is misaligned");
   p.a_codes = a_codes;
   p.a_scales = a_scales;
   p.b_codes = b_codes;
   p.b_scales = b_scales;
   p.a_ts = a_ts;
   p.b_ts = b_ts;
+  return ok();
+}
+
+int gemm_impl(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+              const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts, int64_t M,
+              int64_t N, int64_t K, void *c, int out_dtype, int64_t ldc, void *stream, int if4) {
+  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16)
+    return fail(NVFP4_INVALID_ARG, "out_dtype %d is not NVFP4_F32 or NVFP4_BF16", out_dtype);
+  GemmParams p;
+  int rc = gemm_operands(p, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K);
+  if (rc != NVFP4_OK) return rc;
+  if (ldc < N) return fail(NVFP4_BAD_SHAPE, "ldc %lld < N %lld", (long long)ldc, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  if (!c) return fail(NVFP4_INVALID_ARG, "null device pointer");
+  if (!aligned(c, out_dtype == NVFP4_BF16 ? 2 : 4)) return fail(NVFP4_MISALIGNED, "c is misaligned");
   p.c = c;
   p.ldc = ldc;
-  p.M = (uint32_t)M;
-  p.N = (uint32_t)N;
-  p.K = (uint32_t)K;
-  hipError_t e = launch_gemm(p, out_dtype == NVFP4_BF16, if4, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_gemm(p, out_dtype == NVFP4_BF16 ? kOutBf16 : kOutF32, if4,
+                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -415,6 +429,31 @@ int nvfp4_gemm_if4(const uint8_t *a_codes, const uint8_t *a_scales, const float 
                    void *stream) {
   return gemm_impl(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K, c, out_dtype, ldc,
                    stream, 1);
+}
+
+int nvfp4_gemm_nvfp4_rtn(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+                         const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+                         int64_t M, int64_t N, int64_t K, const float *c_ts, uint8_t *c_codes,
+                         uint8_t *c_scales, float *c_amax, void *stream) {
+  GemmParams p;
+  int rc = gemm_operands(p, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, M, N, K);
+  if (rc != NVFP4_OK) return rc;
+  if (N % 16) return fail(NVFP4_BAD_SHAPE, "N %lld is not a multiple of 16", (long long)N);
+  if (c_amax && !aligned(c_amax, 4)) return fail(NVFP4_MISALIGNED, "c_amax is misaligned");
+  if (M > 0 && N > 0) {
+    if (!c_ts || !c_codes || !c_scales) return fail(NVFP4_INVALID_ARG, "null device pointer");
+    if (!aligned(c_codes, 16) || !aligned(c_scales, 16))
+      return fail(NVFP4_MISALIGNED, "c_codes and c_scales must be 16-byte aligned");
+    if (!aligned(c_ts, 4)) return fail(NVFP4_MISALIGNED, "c_ts is misaligned");
+  }
+  if ((M == 0 || N == 0) && !c_amax) return ok();  // nothing to write
+  p.q_codes = c_codes;
+  p.q_scales = c_scales;
+  p.q_ts = c_ts;
+  p.q_amax = c_amax;
+  hipError_t e = launch_gemm(p, kOutNvfp4, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int nvfp4_rht(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld, int axis,

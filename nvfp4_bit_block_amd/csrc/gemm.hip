@@ -254,6 +254,25 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// NVFP4 round-to-nearest of one 16-block z of C with tensor scale s_t (the
+// quantizer's RTN step: the E4M3 scale e = RNE((max |z| / 6) / s_t), codes
+// of z / (E4M3(e) * s_t) on the E2M1 grid, signed zeros when e = 0).
+// Returns e; folds max |z| into amax.
+__device__ __forceinline__ uint32_t rtn_block16(const float z[16], float s_t, uint32_t &lo, uint32_t &hi,
+                                                float &amax) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(z[i]));
+  amax = fmaxf(amax, a);
+  const uint32_t e = e4m3_rne_sat(div_rn(div_by<6>(a), s_t));
+  const float r = e ? rcp_rn(e4m3_value(e) * s_t) : 0.0f;
+  float y[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = z[i] * r;
+  e2m1x16_rne(y, lo, hi);
+  return e;
+}
+
 // Epilogue.  With B as the first MFMA operand, lane (r32, h) of tile
 // (m, n) holds output row 32m + r32 of the wave tile and, in accumulators
 // 4q .. 4q+3, its columns 32n + 8q + 4h .. +3.  The wave scales and
@@ -262,9 +281,10 @@ __device__ __forceinline__ void chunk(Stage &st, uint32_t c, uint32_t k_next, Ra
 // bytes and eight (bf16) or sixteen (fp32) lanes cover a whole row of the
 // wave tile.  The 16-byte column chunks of a row are XOR-swizzled by the
 // row so that both the writes and the reads spread over all LDS banks.
-template <int OUT_BF16>
+template <int OUT>
 __device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][2], const GemmParams &p, uint32_t m0,
-                                           uint32_t n0, uint32_t w) {
+                                           uint32_t n0, uint32_t w, float &qmax) {
+  constexpr bool OUT_BF16 = OUT == kOutBf16;
   const uint32_t wm = w >> 2, wn = w & 3u;
   const float alpha = (*p.a_ts) * (*p.b_ts);
   // (the lane index is re-derived opaquely, so that the compiler does not
@@ -317,8 +337,8 @@ __device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][
       }
     }
   } else {
-    // fp32: one 32 x 64 half (m) of the wave tile at a time, rows of 256
-    // bytes (16 chunks)
+    // fp32 and NVFP4: one 32 x 64 half (m) of the wave tile at a time, as
+    // fp32 rows of 256 bytes (16 chunks)
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       if (m) __syncthreads();  // the reads of the first half are done
@@ -332,6 +352,29 @@ __device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][
                      acc[m][n][4 * q + 3] * alpha};
         }
       __syncthreads();
+      if (OUT == kOutNvfp4) {
+        // one 16-column block per lane and pass: 32 rows x 4 blocks
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t rl = 16 * i + (lane >> 2), b = lane & 3u;
+          float z[16];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float4 v = *reinterpret_cast<const float4 *>(wbuf + rl * 256 + (((4 * b + c) ^ (rl & 15u)) * 16));
+            z[4 * c] = v.x;
+            z[4 * c + 1] = v.y;
+            z[4 * c + 2] = v.z;
+            z[4 * c + 3] = v.w;
+          }
+          const uint32_t row = row0 + 32 * m + rl, col = col0 + 16 * b;
+          if (row >= p.M || col >= p.N) continue;  // N % 16 == 0: blocks are whole
+          uint32_t lo, hi;
+          const uint32_t e = rtn_block16(z, *p.q_ts, lo, hi, qmax);
+          *reinterpret_cast<uint2 *>(p.q_codes + (size_t)row * (p.N / 2) + col / 2) = make_uint2(lo, hi);
+          p.q_scales[(size_t)row * (p.N / 16) + col / 16] = (uint8_t)e;
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t rl = 4 * i + (lane >> 4), cc = lane & 15u;
@@ -391,7 +434,7 @@ __device__ __forceinline__ void make_panels(Panels &P, const GemmParams &p, uint
   P.h = h;
 }
 
-template <int OUT_BF16, int FAST, int IF4>
+template <int OUT, int FAST, int IF4>
 __global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
   __shared__ Stage st;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -416,6 +459,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
   // chunk 0 in r0, chunk 1 in r1 (loads of chunks past the end re-read the
   // last chunk, unused); sched barriers keep the loads in this order
   Raw r0, r1;
+  float qmax = 0.0f;  // kOutNvfp4: max |C| over this lane's blocks
   if (nfull > 0) {
     load_fast(r0, P, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -485,23 +529,28 @@ __global__ __launch_bounds__(1024, 1) void k_gemm(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    store_tile<OUT_BF16>(st, acc, p, cm0, cn0, w);
+    store_tile<OUT>(st, acc, p, cm0, cn0, w, qmax);
     if (nbid >= nt) break;
     __syncthreads();  // every wave has read its output back before the next tile's stage writes
     bid = nbid;
   }
+  if (OUT == kOutNvfp4 && p.q_amax) {
+    // |C| >= 0, so its fp32 bits order as unsigned integers: one atomic
+    // maximum per wave, whose result does not depend on their order
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, d));
+    if (lane == 0) atomicMax(reinterpret_cast<unsigned int *>(p.q_amax), __float_as_uint(qmax));
+  }
 }
 
-template <int IF4>
-static void launch_fmt(const GemmParams &p, int out_bf16, uint32_t grid, hipStream_t s) {
-  const bool fast = (p.K % 64) == 0;
-  if (out_bf16) {
-    if (fast) hipLaunchKernelGGL((k_gemm<1, 1, IF4>), dim3(grid), dim3(1024), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<1, 0, IF4>), dim3(grid), dim3(1024), 0, s, p);
-  } else {
-    if (fast) hipLaunchKernelGGL((k_gemm<0, 1, IF4>), dim3(grid), dim3(1024), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<0, 0, IF4>), dim3(grid), dim3(1024), 0, s, p);
-  }
+// Clears the maximum that k_gemm<kOutNvfp4> accumulates (a kernel rather
+// than a memset node, so that the call can be captured in a graph).
+__global__ void k_clear_amax(float *amax) { *amax = 0.0f; }
+
+template <int OUT, int IF4>
+static void launch_out(const GemmParams &p, uint32_t grid, hipStream_t s) {
+  if ((p.K % 64) == 0) hipLaunchKernelGGL((k_gemm<OUT, 1, IF4>), dim3(grid), dim3(1024), 0, s, p);
+  else hipLaunchKernelGGL((k_gemm<OUT, 0, IF4>), dim3(grid), dim3(1024), 0, s, p);
 }
 
 // One workgroup per compute unit (the stage takes most of a CU's LDS), a
@@ -515,10 +564,20 @@ static uint32_t gemm_grid(uint32_t tiles) {
   return (g == 0 || tiles <= g) ? tiles : g;
 }
 
-hipError_t launch_gemm(const GemmParams &p, int out_bf16, int if4, hipStream_t s) {
+hipError_t launch_gemm(const GemmParams &p, int out, int if4, hipStream_t s) {
+  if (out == kOutNvfp4 && p.q_amax) hipLaunchKernelGGL(k_clear_amax, dim3(1), dim3(1), 0, s, p.q_amax);
+  if (p.M == 0 || p.N == 0) return hipGetLastError();
   const uint32_t grid = gemm_grid(((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile));
-  if (if4) launch_fmt<1>(p, out_bf16, grid, s);
-  else launch_fmt<0>(p, out_bf16, grid, s);
+  if (out == kOutNvfp4) {
+    if (if4) return hipErrorInvalidValue;
+    launch_out<kOutNvfp4, 0>(p, grid, s);
+  } else if (out == kOutBf16) {
+    if (if4) launch_out<kOutBf16, 1>(p, grid, s);
+    else launch_out<kOutBf16, 0>(p, grid, s);
+  } else {
+    if (if4) launch_out<kOutF32, 1>(p, grid, s);
+    else launch_out<kOutF32, 0>(p, grid, s);
+  }
   return hipGetLastError();
 }
 

@@ -81,15 +81,28 @@ struct DequantParams {
 };
 hipError_t launch_dequant(const DequantParams &p, int out_bf16, hipStream_t s);
 
+enum GemmOut : int {
+  kOutF32 = 0,    // C in fp32 at c (leading dimension ldc)
+  kOutBf16 = 1,   // C in bf16, nearest even
+  kOutNvfp4 = 2   // C coded as NVFP4 RTN along N (q_* fields)
+};
+
 struct GemmParams {
   const uint8_t *a_codes, *a_scales;
   const uint8_t *b_codes, *b_scales;
   const float *a_ts, *b_ts;
   void *c;
   int64_t ldc;
+  // kOutNvfp4: codes [M][N/2] and scales [M][N/16] of C with the tensor
+  // scale *q_ts; q_amax, if not null, receives max |C| (the launch clears it
+  // first).
+  uint8_t *q_codes, *q_scales;
+  const float *q_ts;
+  float *q_amax;
   uint32_t M, N, K;
 };
-// if4: operands may hold IF4 blocks (scale bit 7 = INT flag); 0: NVFP4 only.
-hipError_t launch_gemm(const GemmParams &p, int out_bf16, int if4, hipStream_t s);
+// out: a GemmOut; if4: operands may hold IF4 blocks (scale bit 7 = INT
+// flag), 0: NVFP4 only (kOutNvfp4 is built for NVFP4 operands only).
+hipError_t launch_gemm(const GemmParams &p, int out, int if4, hipStream_t s);
 
 }  // namespace nv4

@@ -41,7 +41,7 @@ def test_header_functions_exported(nv):
 
 def test_version_and_strings(nv):
     L = nv.lib()
-    assert nv.abi_version() == 3
+    assert nv.abi_version() == 4
     for st, text in ((OK, b"ok"), (INVALID, b"invalid argument"), (SHAPE, b"bad shape"),
                      (MISALIGNED, b"misaligned pointer or stride"), (WS_SMALL, b"workspace too small"),
                      (HIP_ERR, b"HIP error"), (UNSUPPORTED, b"unsupported")):
@@ -171,5 +171,13 @@ def test_dequantize_and_gemm_rejections(nv):
     # the 256-row operand panel must fit a 32-bit buffer range
     assert g(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, 8, 16777216, P(FAKE), 0, 8,
              None) == UNSUPPORTED
+    q = L.nvfp4_gemm_nvfp4_rtn
+    ops = [P(FAKE)] * 6
+    assert q(*ops, 8, 24, 64, P(FAKE), P(FAKE), P(FAKE), None, None) == SHAPE        # N % 16
+    assert q(*ops, 8, 32, 40, P(FAKE), P(FAKE), P(FAKE), None, None) == SHAPE        # K % 16
+    assert q(*ops, 8, 32, 64, P(0), P(FAKE), P(FAKE), None, None) == INVALID         # no c_ts
+    assert q(*ops, 8, 32, 64, P(FAKE), P(FAKE + 8), P(FAKE), None, None) == MISALIGNED
+    assert q(*ops, 8, 32, 64, P(FAKE), P(FAKE), P(FAKE), P(FAKE + 2), None) == MISALIGNED
+    assert q(P(0), P(0), P(0), P(0), P(0), P(0), 0, 32, 64, P(0), P(0), P(0), None, None) == OK  # empty
     assert L.nvfp4_rht(P(FAKE), 1, 4, 100, 100, 0, w, P(FAKE), None) == SHAPE
     assert L.nvfp4_rht(P(FAKE), 1, 4, 128, 128, 0, None, P(FAKE), None) == INVALID
