@@ -52,12 +52,20 @@ def test_graph_replays_match_eager(nv):
         nv.quantize_nvfp4(W, rounding="mseden", axis=1, rht_signs=signs, seed=5, out=b["wc"][0],
                           workspace=b["wc"][1])
         nv.gemm_nvfp4(b["dy"][0], b["wc"][0], out=b["dx"])
+        # Y once more, coded as NVFP4 by the GEMM, with max|Y| (cleared by
+        # the call's own kernel: the buffer holds 1e30 before every replay)
+        nv.gemm_nvfp4_rtn(b["x"][0], b["w"][0], yts, amax_out=b["ymax"], out=b["yq"])
+
+    yts = torch.full((1,), 6e-4, dtype=torch.float32, device=dev)
 
     def make():
         return {"xc": bufs(T, D, "mseden", 1), "x": bufs(T, D, "rtn", 0), "w": bufs(O, D, "rtn", 0),
                 "dy": bufs(T, O, "mseden", 0), "wc": bufs(O, D, "mseden", 1),
                 "y": torch.empty((T, O), dtype=torch.float32, device=dev),
-                "dx": torch.empty((T, D), dtype=torch.float32, device=dev)}
+                "dx": torch.empty((T, D), dtype=torch.float32, device=dev),
+                "yq": nv.QTensor(torch.empty((T, O // 2), dtype=torch.uint8, device=dev),
+                                 torch.empty((T, O // 16), dtype=torch.uint8, device=dev), yts),
+                "ymax": torch.empty(1, dtype=torch.float32, device=dev)}
 
     def fill(seed):
         r = np.random.default_rng(seed)
@@ -82,13 +90,16 @@ def test_graph_replays_match_eager(nv):
         for k in ("xc", "x", "w", "dy", "wc"):
             q = b[k][0]
             out += [q.codes, q.scales, q.tensor_scale]
-        return out + [b["y"], b["dx"]]
+        return out + [b["y"], b["dx"], b["yq"].codes, b["yq"].scales, b["ymax"]]
 
     for i in range(4):
         fill(100 + i)
+        gb["ymax"].fill_(1e30)
+        eb["ymax"].fill_(1e30)
         graph.replay()
         torch.cuda.synchronize()
         got = [t.clone() for t in tensors(gb)]
+        assert 0.0 < float(gb["ymax"].cpu()[0]) < 1e29, f"replay {i}: max|Y| was not cleared"
         X.mul_(1.0)                               # eager work between replays
         step(eb)
         torch.cuda.synchronize()
