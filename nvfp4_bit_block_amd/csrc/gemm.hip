@@ -44,7 +44,11 @@
 //
 // Epilogue: the accumulators go through LDS (each wave's 64 x 64 tile in
 // its own 8 KB of the stage) so that the output is written in 16-byte row
-// segments; the next tile's first operand loads are issued before it.
+// segments; the next tile's first operand loads are issued before it.  The
+// output is fp32, bf16, or NVFP4: each 16-column block of a row coded with
+// round-to-nearest under a given tensor scale, the forward pass's coding of
+// the next layer's input (Quartet II news summary, "Quantisierung im
+// Vorwaertsdurchlauf").
 #include "kernels.hpp"
 
 namespace nv4 {
