@@ -22,15 +22,31 @@
 namespace nv4 {
 
 // ---------------------------------------------------------------- helpers
+// This thread's share of the maximum of n <= kMaxPartials partial maxima
+// (all >= 0): its kMaxPartials / kThreads loads are issued together, so the
+// prologue of every workgroup that needs the tensor scale waits on memory
+// once rather than once per load; loads past n read 0 (range-checked).
+__device__ __forceinline__ float partials_max(const float *v, uint32_t n) {
+  static_assert(kMaxPartials % kThreads == 0, "partials per thread");
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)v, (short)0, (int)(4 * n), kRsrcWord3);
+  float m[kMaxPartials / kThreads];
+#pragma unroll
+  for (int k = 0; k < kMaxPartials / kThreads; ++k)
+    m[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (threadIdx.x + k * kThreads), 0, 0));
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMaxPartials / kThreads; ++k) a = fmaxf(a, m[k]);
+  return a;
+}
+
 __device__ __forceinline__ float tensor_scale(const QuantParams &p, float *red) {
   if (p.ts_in) return *p.ts_in;
   if (p.amax_in) {
     const float a = *p.amax_in;
     return (a > 0.0f) ? a / p.top : 1.0f;
   }
-  float m = 0.0f;
-  for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.partial[i]);
-  m = block_max(m, red, kThreads);
+  const float m = block_max(partials_max(p.partial, p.npartial), red, kThreads);
   return (m > 0.0f) ? m / p.top : 1.0f;
 }
 
@@ -669,16 +685,12 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
   if (p.ts_in) {
     s_t = *p.ts_in;
   } else {
-    float m = 0.0f;
-    for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.partial[i]);
-    m = block_max(m, red, kThreads);
+    const float m = block_max(partials_max(p.partial, p.npartial), red, kThreads);
     s_t = (m > 0.0f) ? m / 448.0f : 1.0f;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   if (p.amax_out && blockIdx.x == 0) {
-    float m = 0.0f;
-    for (uint32_t i = threadIdx.x; i < p.npartial; i += kThreads) m = fmaxf(m, p.rpartial[i]);
-    m = block_max(m, red, kThreads);
+    const float m = block_max(partials_max(p.rpartial, p.npartial), red, kThreads);
     if (threadIdx.x == 0) *p.amax_out = m;
   }
   // Whole calls (8 blocks each): the next call's targets are loaded while
