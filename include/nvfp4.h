@@ -106,8 +106,10 @@ typedef struct nvfp4_opts {
   uint64_t seed;           /* Philox-4x32-10 key                               */
   uint32_t stream;         /* Philox counter word 3 (e.g. a step or trial id)  */
   int32_t eden_group;      /* MS-EDEN correction group: 128 (default) or 16    */
-  const float *tensor_scale_in; /* DEVICE pointer to a given fp32 tensor scale,
-                              or NULL to compute it from this tensor           */
+  const float *tensor_scale_in; /* DEVICE pointer to a given fp32 tensor scale
+                              (positive and finite, else the codes are
+                              unspecified), or NULL to compute it from this
+                              tensor                                           */
   int32_t scale_rule;      /* nvfp4_scale_rule; other than MAX6 needs RTN      */
   float *amax_out;         /* DEVICE fp32 or NULL.  MS-EDEN with a computed
                               tensor scale also writes max|x| of the input as
@@ -281,7 +283,9 @@ int nvfp4_gemm_if4(const uint8_t *a_codes, const uint8_t *a_scales, const float 
  * is the next layer's NVFP4 input without writing or re-reading C.
  * c_ts: DEVICE fp32, the tensor scale to code with (max |C| is not known
  * before C is computed, so it comes from the caller, e.g. from c_amax of an
- * earlier step divided by 6 * 448).  c_codes: DEVICE [M x N/2] bytes,
+ * earlier step divided by 6 * 448); it must be positive and finite, else
+ * the codes are unspecified (the value is on the device, so no error is
+ * returned for it).  c_codes: DEVICE [M x N/2] bytes,
  * c_scales: DEVICE [M x N/16] bytes, both 16-byte aligned, as the
  * quantizer's output for rows_out = M, K = N.  c_amax: DEVICE fp32 or NULL;
  * receives max |C| over all entries (cleared by the call itself).
