@@ -225,7 +225,11 @@ int nvfp4_quantize_if4(const void *x, int in_dtype, int64_t rows, int64_t cols, 
                        float *tensor_scale, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Dequantization, the inverse of the encodings above: out[r][k] =
+ * Dequantization [PAL opening paragraph (the sixteen E2M1 values and the
+ * per-block scale they are multiplied by); IF4 Figure 1 (a block flagged INT
+ * in the scale's sign bit holds integers instead of E2M1 values); QII-sum
+ * "Quantisierung im Vorwaertsdurchlauf" (E4M3 block scale times the fp32
+ * tensor scale)]: out[r][k] =
  * sign * (v * (E4M3(scale & 0x7F) * tensor_scale)), v the E2M1 value or, for
  * IF4 groups with bit 7 set, the integer magnitude; then, if inv_rht_signs is
  * not NULL, the inverse rotation signs * (2^-3.5 * H_128 * z) of every
@@ -300,8 +304,12 @@ int nvfp4_gemm_nvfp4_rtn(const uint8_t *a_codes, const uint8_t *a_scales, const 
                          uint8_t *c_scales, float *c_amax, void *stream);
 
 /*
- * The rotation alone, for checking it: out[rows_out x K] fp32 = the rotated
- * values of step 1 of nvfp4_quantize_nvfp4, in the output layout of `axis`.
+ * The randomized Hadamard rotation alone [QII-sum "Quantisierung im
+ * Rueckwaertsdurchlauf" (the backward operands are rotated along the
+ * micro-scaling groups before MS-EDEN); PAL opening paragraph (a random
+ * sign flip followed by a Hadamard transform)], for checking it:
+ * out[rows_out x K] fp32 = the rotated values of step 1 of
+ * nvfp4_quantize_nvfp4, in the output layout of `axis`.
  * Same x rules; K % 128 == 0; out device, 16-byte aligned.
  */
 int nvfp4_rht(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld, int axis,

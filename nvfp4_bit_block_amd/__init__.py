@@ -135,6 +135,73 @@ def _dtype_code(t, torch):
     raise NvFp4Error(f"input dtype {t.dtype} is not float32 or bfloat16")
 
 
+def _check_tensor(t, name, shape=None, dtypes=None, dev=None, dense=False, min_numel=None, where=True):
+    """Host-side checks of a tensor handed to the library (the C ABI sees
+    raw pointers only, so a wrong size or layout would become an
+    out-of-bounds device access).  Shape, dtype and layout are checked
+    before the device, so that the messages name the first real problem."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise NvFp4Error(f"{name} must be a torch tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise NvFp4Error(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise NvFp4Error(f"{name} holds {t.numel()} elements, at least {min_numel} needed")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise NvFp4Error(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if dense and not t.is_contiguous():
+        raise NvFp4Error(f"{name} must be contiguous")
+    if where:
+        _check_where(t, name, dev)
+
+
+def _check_where(t, name, dev=None):
+    if not t.is_cuda:
+        raise NvFp4Error(f"{name} must be a device tensor")
+    if dev is not None and t.device != dev:
+        raise NvFp4Error(f"{name} is on {t.device}, expected {dev}")
+
+
+def _check_input(x, name="x"):
+    """A 2-D float32/bfloat16 input with unit stride along its last axis."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise NvFp4Error(f"{name} must be a 2-D torch tensor")
+    if x.size(1) > 1 and x.stride(1) != 1:
+        raise NvFp4Error(f"{name} must have unit stride along its last dimension")
+    if x.size(0) > 1 and x.stride(0) < x.size(1):
+        raise NvFp4Error(f"{name} has a row stride below its row length")
+    _check_tensor(x, name, dtypes=(torch.float32, torch.bfloat16))
+
+
+def _check_qtensor(q, name, rows=None, k=None, dev=None):
+    """A packed tensor: codes [rows, k/2] and scales [rows, k/16] uint8,
+    contiguous, and a float32 tensor scale, all on one device."""
+    import torch
+    if not isinstance(q, QTensor):
+        raise NvFp4Error(f"{name} must be a QTensor")
+    if q.codes.dim() != 2 or q.scales.dim() != 2:
+        raise NvFp4Error(f"{name}: codes and scales must be 2-D")
+    r = q.codes.shape[0] if rows is None else rows
+    kk = q.codes.shape[1] * 2 if k is None else k
+    if kk % 16:
+        raise NvFp4Error(f"{name}: K = {kk} is not a multiple of 16")
+    dev = q.codes.device if dev is None else dev
+    parts = ((q.codes, f"{name}.codes", dict(shape=(r, kk // 2), dtypes=(torch.uint8,), dense=True)),
+             (q.scales, f"{name}.scales", dict(shape=(r, kk // 16), dtypes=(torch.uint8,), dense=True)),
+             (q.tensor_scale, f"{name}.tensor_scale", dict(dtypes=(torch.float32,), min_numel=1)))
+    for t, n, kw in parts:   # shapes and layouts first, then where the parts live
+        _check_tensor(t, n, where=False, **kw)
+    for t, n, _ in parts:
+        _check_where(t, n, dev)
+
+
+def _check_scalar(t, name, dev):
+    import torch
+    if t is not None:
+        _check_tensor(t, name, dtypes=(torch.float32,), dev=dev, min_numel=1)
+
+
 _SCALE_RULE = {"max6": SCALE_MAX6, "4over6": SCALE_4OVER6, "four_over_six": SCALE_4OVER6,
                "search": SCALE_SEARCH, SCALE_MAX6: SCALE_MAX6, SCALE_4OVER6: SCALE_4OVER6,
                SCALE_SEARCH: SCALE_SEARCH}
@@ -190,30 +257,28 @@ def _quantize(fn, x, rounding, axis, rht_signs, seed, stream_id, eden_group, ten
               out, workspace, fmt, scale_rule=SCALE_MAX6, amax_out=None, amax_in=None):
     import torch
     L = lib()
-    if x.dim() != 2:
-        raise NvFp4Error("x must be 2-D")
-    if not x.is_cuda:
-        raise NvFp4Error("x must be a device tensor")
-    if x.size(1) > 1 and x.stride(1) != 1:
-        raise NvFp4Error("x must have unit stride along its last dimension")
+    _check_input(x)
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
-    for t in (amax_out, amax_in):
-        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or t.numel() < 1):
-            raise NvFp4Error("amax_out / amax_in must be float32 device tensors of at least one element")
+    dev = x.device
+    for t, n in ((amax_out, "amax_out"), (amax_in, "amax_in"), (tensor_scale_in, "tensor_scale_in")):
+        _check_scalar(t, n, dev)
     o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule,
               amax_out, amax_in)
     R, K = (rows, cols) if axis == 0 else (cols, rows)
-    dev = x.device
     if out is None:
         out = QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
                       torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
                       torch.empty(1, dtype=torch.float32, device=dev), fmt)
     else:
+        if K % 16 == 0:
+            _check_qtensor(out, "out", rows=R, k=K, dev=dev)
         out.format = fmt
     wsz = int(L.nvfp4_workspace_size(rows, cols, ctypes.byref(o)))
     if workspace is None or workspace.numel() < wsz:
         workspace = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+    else:
+        _check_tensor(workspace, "workspace", dtypes=(torch.uint8,), dev=dev, dense=True)
     rc = fn(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld, ctypes.byref(o),
             ctypes.c_void_p(out.codes.data_ptr()), ctypes.c_void_p(out.scales.data_ptr()),
             ctypes.c_void_p(out.tensor_scale.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
@@ -245,12 +310,12 @@ def quantize_nvfp4_dual(x, rht_signs=None, seed=0, stream_id=0, eden_group=128, 
     rounding "mseden" and axis 0 / axis 1."""
     import torch
     L = lib()
-    if x.dim() != 2 or not x.is_cuda or (x.size(1) > 1 and x.stride(1) != 1):
-        raise NvFp4Error("x must be a 2-D device tensor with unit stride along its last dimension")
+    _check_input(x)
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
-    o = _opts(MSEDEN, 0, rht_signs, seed, stream_id, eden_group, tensor_scale_in)
     dev = x.device
+    _check_scalar(tensor_scale_in, "tensor_scale_in", dev)
+    o = _opts(MSEDEN, 0, rht_signs, seed, stream_id, eden_group, tensor_scale_in)
 
     def alloc(R, K):
         return QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
@@ -258,9 +323,14 @@ def quantize_nvfp4_dual(x, rht_signs=None, seed=0, stream_id=0, eden_group=128, 
                        torch.empty(1, dtype=torch.float32, device=dev), FORMAT_NVFP4)
     qr = out_rows if out_rows is not None else alloc(rows, cols)
     qc = out_cols if out_cols is not None else alloc(cols, rows)
+    if rows % 16 == 0 and cols % 16 == 0:
+        _check_qtensor(qr, "out_rows", rows=rows, k=cols, dev=dev)
+        _check_qtensor(qc, "out_cols", rows=cols, k=rows, dev=dev)
     wsz = int(L.nvfp4_workspace_size_dual(rows, cols, ctypes.byref(o)))
     if workspace is None or workspace.numel() < wsz:
         workspace = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+    else:
+        _check_tensor(workspace, "workspace", dtypes=(torch.uint8,), dev=dev, dense=True)
     rc = L.nvfp4_quantize_nvfp4_dual(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld,
                                      ctypes.byref(o), ctypes.c_void_p(qr.codes.data_ptr()),
                                      ctypes.c_void_p(qr.scales.data_ptr()),
@@ -287,9 +357,13 @@ def dequantize(q, inv_rht_signs=None, out_dtype=None, out=None):
     """Decode a QTensor to [rows_out, K] float32 (or bfloat16), optionally
     undoing the rotation."""
     import torch
+    _check_qtensor(q, "q")
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((q.rows, q.k), dtype=out_dtype, device=q.codes.device)
+    else:
+        _check_tensor(out, "out", shape=(q.rows, q.k), dtypes=(torch.float32, torch.bfloat16),
+                      dev=q.codes.device, dense=True)
     w = None
     if inv_rht_signs is not None:
         w = signs_to_words(inv_rht_signs)
@@ -305,6 +379,8 @@ def gemm_nvfp4(a, b, out_dtype=None, out=None):
     """C = (ts_a ts_b) * A_hat @ B_hat^T for two K-major NVFP4 or IF4
     QTensors (A: [M, K], B: [N, K]); C is [M, N] float32 (or bfloat16)."""
     import torch
+    _check_qtensor(a, "a")
+    _check_qtensor(b, "b", dev=a.codes.device)
     if a.k != b.k:
         raise NvFp4Error(f"K mismatch: {a.k} vs {b.k}")
     if a.format not in (FORMAT_NVFP4, FORMAT_IF4) or b.format not in (FORMAT_NVFP4, FORMAT_IF4):
@@ -315,6 +391,10 @@ def gemm_nvfp4(a, b, out_dtype=None, out=None):
     M, N = a.rows, b.rows
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    else:
+        _check_tensor(out, "out", shape=(M, N), dtypes=(torch.float32, torch.bfloat16), dev=a.codes.device)
+        if (N > 1 and out.stride(1) != 1) or (M > 1 and out.stride(0) < N):
+            raise NvFp4Error("out must have unit stride along its last dimension and a row stride >= N")
     ldc = out.stride(0) if M > 1 else N
     rc = fn(ctypes.c_void_p(a.codes.data_ptr()), ctypes.c_void_p(a.scales.data_ptr()),
                                 ctypes.c_void_p(a.tensor_scale.data_ptr()),
@@ -333,18 +413,23 @@ def gemm_nvfp4_rtn(a, b, tensor_scale, amax_out=None, out=None):
     amax_out (float32 device [1]) receives max |C|.  `out` may give a
     preallocated QTensor."""
     import torch
+    _check_qtensor(a, "a")
+    dev = a.codes.device
+    _check_qtensor(b, "b", dev=dev)
     if a.k != b.k:
         raise NvFp4Error(f"K mismatch: {a.k} vs {b.k}")
     if a.format != FORMAT_NVFP4 or b.format != FORMAT_NVFP4:
         raise NvFp4Error("operands must be NVFP4 QTensors")
-    for t in (tensor_scale, amax_out):
-        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or t.numel() < 1):
-            raise NvFp4Error("tensor_scale and amax_out must be float32 device tensors")
+    if tensor_scale is None:
+        raise NvFp4Error("tensor_scale is required")
+    _check_scalar(tensor_scale, "tensor_scale", dev)
+    _check_scalar(amax_out, "amax_out", dev)
     M, N = a.rows, b.rows
     if out is None:
-        dev = a.codes.device
         out = QTensor(torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
                       torch.empty((M, N // 16), dtype=torch.uint8, device=dev), tensor_scale, FORMAT_NVFP4)
+    elif N % 16 == 0:
+        _check_qtensor(out, "out", rows=M, k=N, dev=dev)
     rc = lib().nvfp4_gemm_nvfp4_rtn(
         ctypes.c_void_p(a.codes.data_ptr()), ctypes.c_void_p(a.scales.data_ptr()),
         ctypes.c_void_p(a.tensor_scale.data_ptr()), ctypes.c_void_p(b.codes.data_ptr()),
@@ -359,10 +444,13 @@ def gemm_nvfp4_rtn(a, b, tensor_scale, amax_out=None, out=None):
 def rht(x, signs, axis=0, out=None):
     """The rotation step alone: rotated fp32 values [rows_out, K]."""
     import torch
+    _check_input(x)
     rows, cols = x.shape
     R, K = (rows, cols) if axis == 0 else (cols, rows)
     if out is None:
         out = torch.empty((R, K), dtype=torch.float32, device=x.device)
+    else:
+        _check_tensor(out, "out", shape=(R, K), dtypes=(torch.float32,), dev=x.device, dense=True)
     w = signs_to_words(signs)
     ld = x.stride(0) if rows > 1 else cols
     rc = lib().nvfp4_rht(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld, int(axis),

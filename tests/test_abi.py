@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -181,3 +182,51 @@ def test_dequantize_and_gemm_rejections(nv):
     assert q(P(0), P(0), P(0), P(0), P(0), P(0), 0, 32, 64, P(0), P(0), P(0), None, None) == OK  # empty
     assert L.nvfp4_rht(P(FAKE), 1, 4, 100, 100, 0, w, P(FAKE), None) == SHAPE
     assert L.nvfp4_rht(P(FAKE), 1, 4, 128, 128, 0, None, P(FAKE), None) == INVALID
+
+
+# ---------------------------------------------------------------- the binding's own checks
+# The C ABI sees raw pointers only, so the Python binding checks every tensor
+# it hands over (shape, dtype, layout, device) and raises before any call;
+# these cases need no GPU: host tensors are rejected as such, and wrongly
+# shaped ones by their shape before the device is looked at.
+
+def _raises(nv, fn, match):
+    with pytest.raises(nv.NvFp4Error, match=match):
+        fn()
+
+
+def test_binding_rejects_host_and_misshaped_tensors(nv):
+    import torch
+    x = torch.zeros((64, 256), dtype=torch.bfloat16)
+    _raises(nv, lambda: nv.quantize_nvfp4(x), "device tensor")
+    _raises(nv, lambda: nv.quantize_nvfp4(x[:, ::2]), "unit stride")
+    _raises(nv, lambda: nv.quantize_nvfp4(torch.zeros(64, 256, 2)), "2-D")
+    _raises(nv, lambda: nv.quantize_nvfp4(torch.zeros((64, 256), dtype=torch.float16)), "dtype")
+    _raises(nv, lambda: nv.rht(x, np.zeros(128, np.uint8)), "device tensor")
+    _raises(nv, lambda: nv.rht(x.t(), np.zeros(128, np.uint8)), "unit stride")
+    # a caller-supplied output of the wrong shape, dtype or layout
+    good = nv.QTensor(torch.zeros((64, 128), dtype=torch.uint8), torch.zeros((64, 16), dtype=torch.uint8),
+                      torch.zeros(1))
+    bad_codes = nv.QTensor(torch.zeros((64, 64), dtype=torch.uint8), good.scales, good.tensor_scale)
+    bad_scales = nv.QTensor(good.codes, torch.zeros((16, 64), dtype=torch.uint8), good.tensor_scale)
+    bad_dtype = nv.QTensor(good.codes.to(torch.int32), good.scales, good.tensor_scale)
+    strided = nv.QTensor(torch.zeros((64, 256), dtype=torch.uint8)[:, ::2], good.scales, good.tensor_scale)
+    bad_ts = nv.QTensor(good.codes, good.scales, torch.zeros(1, dtype=torch.float64))
+    for q, msg in ((bad_codes, "codes has shape"), (bad_scales, "scales has shape"),
+                   (bad_dtype, "codes has dtype"), (strided, "contiguous"), (bad_ts, "tensor_scale has dtype")):
+        _raises(nv, lambda: nv.quantize_nvfp4(x, out=q), "device tensor")   # the input is checked first
+        _raises(nv, lambda: nv._check_qtensor(q, "out", rows=64, k=256), msg)
+        _raises(nv, lambda: nv.dequantize(q) if q is not bad_codes else nv._check_qtensor(q, "q", k=256), msg)
+    # correct shapes on the host: rejected for their device
+    _raises(nv, lambda: nv.dequantize(good), "device tensor")
+    _raises(nv, lambda: nv.gemm_nvfp4(good, good), "device tensor")
+    _raises(nv, lambda: nv.gemm_nvfp4_rtn(good, good, torch.ones(1)), "device tensor")
+    # GEMM and dequantize outputs
+    _raises(nv, lambda: nv._check_tensor(torch.zeros(64, 63), "out", shape=(64, 64)), "shape")
+    _raises(nv, lambda: nv._check_tensor(torch.zeros(64, 64, dtype=torch.float16), "out",
+                                         dtypes=(torch.float32, torch.bfloat16)), "dtype")
+    _raises(nv, lambda: nv._check_tensor(torch.zeros(1), "tensor_scale", min_numel=2), "at least")
+    _raises(nv, lambda: nv._check_tensor(torch.zeros(64, 64).t(), "out", dense=True), "contiguous")
+    _raises(nv, lambda: nv._check_qtensor(nv.QTensor(torch.zeros((4, 4), dtype=torch.uint8),
+                                                      torch.zeros((4, 1), dtype=torch.uint8), torch.zeros(1)),
+                                          "a"), "multiple of 16")
