@@ -88,20 +88,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def build_divcheck(verbose: bool = False) -> str:
-    """tests/_build/libdivcheck.so: the device check of the refined division
-    (test infrastructure; see tests/divcheck.hip)."""
+def build_test_lib(name: str, verbose: bool = False) -> str:
+    """tests/_build/lib<name>.so from tests/<name>.hip: device checks of the
+    library's arithmetic (test infrastructure; built with the library's own
+    flags and headers, so that they run the kernels' code paths)."""
     tests = os.path.join(os.path.dirname(HERE), "tests")
     out_dir = os.path.join(tests, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    so = os.path.join(out_dir, "libdivcheck.so")
-    obj = os.path.join(out_dir, "divcheck.o")
-    cmd = [_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(tests, "divcheck.hip"), "-o", obj]
+    so = os.path.join(out_dir, f"lib{name}.so")
+    obj = os.path.join(out_dir, f"{name}.o")
+    cmd = [_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(tests, f"{name}.hip"),
+                                     "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for divcheck.hip:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {name}.hip:\n{r.stdout}\n{r.stderr}")
     tdir = _torch_lib_dir()
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     link = ["g++", "-shared", "-o", so + ".tmp", obj]
@@ -112,6 +114,14 @@ def build_divcheck(verbose: bool = False) -> str:
     subprocess.run(link, check=True)
     os.replace(so + ".tmp", so)
     return so
+
+
+TEST_LIBS = ("divcheck", "convcheck")
+
+
+def build_test_libs(verbose: bool = False):
+    with ThreadPoolExecutor(max_workers=len(TEST_LIBS)) as ex:
+        return list(ex.map(lambda n: build_test_lib(n, verbose), TEST_LIBS))
 
 
 if __name__ == "__main__":

@@ -53,8 +53,6 @@
 
 namespace nv4 {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -101,48 +99,6 @@ __device__ __forceinline__ void load_generic(Raw &r, const Panels &p, uint32_t k
   r.scale = s;
 }
 
-// 8 codes (element 2i in the low nibble of byte i) times one fp16 scale.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 s) {
-  const half2_t s2 = {s, s};
-  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// IF4 operands: a block whose scale byte has bit 7 set holds sign-magnitude
-// integers 0..7 instead of E2M1 codes.  Every magnitude of either kind is an
-// fp16 value with a zero low byte, so one byte permute per pair of codes
-// looks up the high bytes in a 16-byte table chosen by the block's flag:
-//   E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6} -> 00 38 3C 3E 40 42 44 46
-//   INT  {0, 1, 2, 3, 4, 5, 6, 7}    -> 00 3C 40 42 44 45 46 47
-constexpr uint32_t kLutFpLo = 0x3E3C3800u, kLutFpHi = 0x46444240u;
-constexpr uint32_t kLutIntLo = 0x42403C00u, kLutIntHi = 0x47464544u;
-
-// 8 codes of one block (element 2i in the low nibble of byte i), decoded
-// through the table {lut_hi:lut_lo}, times one fp16 scale.
-__device__ __forceinline__ half8_t dequant8_lut(uint32_t w, _Float16 s, uint32_t lut_lo, uint32_t lut_hi) {
-  const half2_t s2 = {s, s};
-  const uint32_t lo_n = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-  const uint32_t hi_n = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-  half8_t out;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // bytes [0, code 2k, 0, code 2k+1]
-    const uint32_t h = __builtin_amdgcn_perm(hi_n, lo_n, 0x000C000Cu | ((4u + k) << 24) | ((uint32_t)k << 8));
-    // selector [zero, magnitude, zero, magnitude] -> fp16 magnitudes
-    const uint32_t sel = (h & 0x07000700u) | 0x000C000Cu;
-    const uint32_t mag = __builtin_amdgcn_perm(lut_hi, lut_lo, sel);
-    // sign bits 11 and 27 of h move to the fp16 sign bits 15 and 31
-    const uint32_t v = ((h << 4) & 0x80008000u) | mag;
-    const half2_t p = __builtin_bit_cast(half2_t, v) * s2;
-    out[2 * k] = p[0];
-    out[2 * k + 1] = p[1];
-  }
-  return out;
-}
-
 // LDS stage: [buffer][fragment 0..15 (A 0..7, B 8..15)][step][lane] x 16 bytes.
 typedef half8_t Stage[2][16][kSteps][64];
 static_assert(sizeof(Stage) == 16 * 8192, "the epilogue gives each of the 16 waves 8 KB of the stage");
@@ -160,9 +116,9 @@ __device__ __forceinline__ void scales16(const Raw &r, uint32_t h, Scales<IF4> &
   const uint32_t b = r.scale >> (16 * h);
   if (IF4) {
     sc.f = b;
-    sc.s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b & 0x7F7Fu, 1.0f, false);
+    sc.s = e4m3x2_f16(b & 0x7F7Fu);
   } else {
-    sc.s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+    sc.s = e4m3x2_f16(b);
   }
 }
 

@@ -49,6 +49,10 @@ def lib():
     for name in ("orc_sr_e2m1", "orc_sr_e4m3"):
         getattr(L, name).restype = _INT
         getattr(L, name).argtypes = [_F32, _U32]
+    L.orc_e2m1_rne_run.restype = None
+    L.orc_e2m1_rne_run.argtypes = [_U32, _U64, _P]
+    L.orc_e4m3_run.restype = None
+    L.orc_e4m3_run.argtypes = [_U32, _U64, _INT, _P]
     L.orc_philox4x32_10.restype = None
     L.orc_philox4x32_10.argtypes = [_P, _P, _P]
     L.orc_uniform16.restype = _U32
@@ -123,6 +127,22 @@ def sr_e2m1(a, u16):
 
 def sr_e4m3(a, u16):
     return int(lib().orc_sr_e4m3(float(a), int(u16)))
+
+
+def e2m1_rne_run(bits_lo, count):
+    """Packed RTN nibbles of the fp32 bit patterns bits_lo .. bits_lo+count-1
+    (sign<<3 | E2M1_RNE(min(|y|, 6)), two per byte)."""
+    out = np.empty(count // 2, dtype=np.uint8)
+    lib().orc_e2m1_rne_run(int(bits_lo), int(count), _ptr(out))
+    return out
+
+
+def e4m3_run(bits_lo, count, ceil_mode=False):
+    """E4M3 bytes (RNE, or rounded up) of the fp32 bit patterns
+    bits_lo .. bits_lo+count-1."""
+    out = np.empty(count, dtype=np.uint8)
+    lib().orc_e4m3_run(int(bits_lo), int(count), int(bool(ceil_mode)), _ptr(out))
+    return out
 
 
 def philox4x32_10(ctr, key):

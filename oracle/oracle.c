@@ -165,6 +165,37 @@ int orc_sr_e4m3(float a, uint32_t u16) {
   return ((float)u16 < p * 65536.0f) ? j + 1 : j;
 }
 
+/* Array forms of the rules above, over a run of consecutive fp32 bit
+ * patterns (bits_lo, bits_lo + 1, ...), for the exhaustive comparison with
+ * the device's conversions: no arithmetic beyond the functions they loop.
+ *   codes: the nibble of an RTN-coded value y as the block coding below
+ *          forms it, sign<<3 | E2M1_RNE(min(|y|, 6)), two per byte (even
+ *          pattern in the low nibble); count even.
+ *   bytes: E4M3 byte of v by RNE (ceil_mode 0) or rounded up (1). */
+void orc_e2m1_rne_run(uint32_t bits_lo, uint64_t count, uint8_t *codes) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)(count / 2); i++) {
+    int nib[2];
+    for (int j = 0; j < 2; j++) {
+      uint32_t b = bits_lo + (uint32_t)(2 * i + j);
+      float y;
+      memcpy(&y, &b, sizeof(y));
+      nib[j] = (signbit(y) ? 8 : 0) | orc_e2m1_rne(fminf(fabsf(y), 6.0f));
+    }
+    codes[i] = (uint8_t)(nib[0] | (nib[1] << 4));
+  }
+}
+
+void orc_e4m3_run(uint32_t bits_lo, uint64_t count, int ceil_mode, uint8_t *bytes) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)count; i++) {
+    uint32_t b = bits_lo + (uint32_t)i;
+    float v;
+    memcpy(&v, &b, sizeof(v));
+    bytes[i] = (uint8_t)(ceil_mode ? orc_e4m3_ceil_sat(v) : orc_e4m3_rne_sat(v));
+  }
+}
+
 /* ======================================================================
  * Counter-based RNG: Philox-4x32 with 10 rounds [Philox].
  * Each round multiplies words 0 and 2 by the two round multipliers, swaps
