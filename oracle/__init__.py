@@ -49,6 +49,8 @@ def lib():
     for name in ("orc_sr_e2m1", "orc_sr_e4m3"):
         getattr(L, name).restype = _INT
         getattr(L, name).argtypes = [_F32, _U32]
+    L.orc_sr_expected_sq.restype = _F32
+    L.orc_sr_expected_sq.argtypes = [_F32, _INT]
     L.orc_e2m1_rne_run.restype = None
     L.orc_e2m1_rne_run.argtypes = [_U32, _U64, _P]
     L.orc_e4m3_run.restype = None
@@ -127,6 +129,11 @@ def sr_e2m1(a, u16):
 
 def sr_e4m3(a, u16):
     return int(lib().orc_sr_e4m3(float(a), int(u16)))
+
+
+def sr_expected_sq(a, is_int=False):
+    """(a - l)(u - a) on the E2M1 grid (or integers 0..7), fp32."""
+    return float(lib().orc_sr_expected_sq(float(a), int(bool(is_int))))
 
 
 def e2m1_rne_run(bits_lo, count):

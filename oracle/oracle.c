@@ -165,6 +165,25 @@ int orc_sr_e4m3(float a, uint32_t u16) {
   return ((float)u16 < p * 65536.0f) ? j + 1 : j;
 }
 
+/* Scaled-INT4 magnitudes as a grid, for stochastic rounding onto integers. */
+static const float GRID_INT4[8] = {0.0f, 1.0f, 2.0f, 3.0f, 4.0f, 5.0f, 6.0f, 7.0f};
+
+/* Expected squared error, in grid units, of stochastically rounding a onto
+ * an ascending grid: (a - l)(u - a) with l <= a < u the bracketing points
+ * [PAL opening paragraph: SR's error for a value between two levels]; 0 at
+ * the top of the grid, which a value there keeps.
+ * Pinned by: exact enumeration of all 65536 uniforms of sr_on_grid. */
+static float sr_expected_sq(const float *grid, int n, float a) {
+  if (a >= grid[n - 1]) return 0.0f;
+  int j = 0;
+  while (j < n - 1 && grid[j + 1] <= a) j++;
+  return (a - grid[j]) * (grid[j + 1] - a);
+}
+
+float orc_sr_expected_sq(float a, int is_int) {
+  return sr_expected_sq(is_int ? GRID_INT4 : GRID_E2M1, 8, a);
+}
+
 /* Array forms of the rules above, over a run of consecutive fp32 bit
  * patterns (bits_lo, bits_lo + 1, ...), for the exhaustive comparison with
  * the device's conversions: no arithmetic beyond the functions they loop.
@@ -383,6 +402,55 @@ static void if4_block(const float *z, float s_t, int format, uint8_t *codes_row,
   for (int i = 0; i < 16; i++) put_nibble(codes_row, k0 + i, use_int ? ni[i] : nf[i]);
 }
 
+/* One stochastic-rounding candidate of a 16-block: the scale byte e =
+ * E4M3 rounded up of (a/top)/s_t (so that nothing clips, as for NVFP4 SR),
+ * S = value(e) * s_t, y_i = min(|z_i| / S, top), and the closed-form expected
+ * squared error of the block, (S * S) * pairwise sum of (y - l)(u - y). */
+static int sr_candidate(const float *z, float s_t, int is_int, float y[16], float *ese) {
+  const float top = is_int ? 7.0f : 6.0f;
+  const float *grid = is_int ? GRID_INT4 : GRID_E2M1;
+  float a = 0.0f;
+  for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(z[i]));
+  int e = orc_e4m3_ceil_sat((a / top) / s_t);
+  float S = orc_e4m3_value(e) * s_t;
+  float r = (e != 0) ? 1.0f / S : 0.0f;
+  float d[16];
+  for (int i = 0; i < 16; i++) {
+    y[i] = (e != 0) ? fminf(fabsf(z[i] * r), top) : 0.0f;
+    d[i] = sr_expected_sq(grid, 8, y[i]);
+  }
+  *ese = (S * S) * orc_pairwise_sum(d, 16);
+  return e;
+}
+
+/* IF4 with stochastic rounding, for gradients [IF4 page, Figure 4: IF4 also
+ * pays in the backward pass, more so with MS-EDEN; IF4 abstract and Figure 1
+ * for the per-16 FP4/INT4 choice in the scale's sign bit; PAL opening
+ * paragraph for SR and its error (y - l)(u - y)].
+ * READING: both branches are NVFP4-SR-like: E4M3 scale rounded up from a/6
+ * (E2M1 grid) and from a/7 (integers 0..7) under the shared tensor scale,
+ * elements rounded stochastically with the same uniform whichever branch is
+ * kept; the branch is chosen BEFORE rounding, by the smaller closed-form
+ * expected squared error (tie: FP4), so the choice does not depend on the
+ * random draw and each element stays unbiased.
+ * Pinned by: the exact expectation over all 65536 uniforms of the chosen
+ * branch is the smaller one; Monte-Carlo unbiasedness; expected error never
+ * above NVFP4 SR's (its FP4 branch is NVFP4 SR). */
+static void if4_sr_block(const float *z, float s_t, uint64_t seed, uint32_t stream, uint64_t idx0,
+                         uint8_t *codes_row, int64_t k0, uint8_t *scale_out) {
+  float yf[16], yi[16], ese_f, ese_i;
+  int ef = sr_candidate(z, s_t, 0, yf, &ese_f);
+  int ei = sr_candidate(z, s_t, 1, yi, &ese_i);
+  int use_int = ese_i < ese_f;
+  *scale_out = (uint8_t)(use_int ? (ei | 0x80) : ef);
+  for (int i = 0; i < 16; i++) {
+    uint32_t u = orc_uniform16(seed, 0, stream, idx0 + (uint64_t)i);
+    int mag = use_int ? (ei ? sr_on_grid(GRID_INT4, 8, yi[i], u) : 0)
+                      : (ef ? orc_sr_e2m1(yf[i], u) : 0);
+    put_nibble(codes_row, k0 + i, (signbit(z[i]) ? 8 : 0) | mag);
+  }
+}
+
 /* Four Over Six, the local scaling option of the forward pass
  * [QII-sum "Quantisierung im Vorwaertsdurchlauf"; IF4 Table 1, row
  * "NVFP4 (4/6)": maximum 6 x 256, relative dynamic range 57.1 %].
@@ -497,6 +565,61 @@ static void eden_group(const float *z, int G, uint8_t *codes_row, int64_t k0, fl
   for (int b = 0; b < G / 16; b++) tb[b] = s_b[b] * c;
 }
 
+/* IF4 with MS-EDEN, first half [IF4 page, Figure 4 (IF4 with MS-EDEN in
+ * the backward pass); QII-abs and QII-sum "Quantisierung im
+ * Rueckwaertsdurchlauf" for MS-EDEN].
+ * READING: every 16-block is coded by RTN twice under its exact scales,
+ * E2M1 under a/6 and integers 0..7 under a/7, and keeps the branch with the
+ * smaller pairwise squared error (tie: FP4), as IF4 RTN does; the EDEN
+ * correction c = sum z^2 / sum z*zhat runs over the group with the kept
+ * reconstructions; t_b = (kept exact scale) * c; the INT choice goes to
+ * flag[b] (bit 7 of the scale byte).  EDEN's correction makes the rotated
+ * estimate unbiased for any deterministic coding of the group, so the
+ * choice keeps it unbiased.
+ * Pinned by: unbiasedness under Haar-random rotations and under the RHT
+ * (Monte Carlo); the kept branch is the float64 minimum; lower error than
+ * NVFP4 MS-EDEN on rotated Gaussian data. */
+static void eden_group_if4(const float *z, int G, uint8_t *codes_row, int64_t k0, float *tb,
+                           uint8_t *flag) {
+  float zz[128] = {0}, zh[128] = {0}, s_b[8] = {0};
+  for (int b = 0; b < G / 16; b++) {
+    const float *zb = z + 16 * b;
+    float a = 0.0f;
+    for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(zb[i]));
+    const float s_f = a / 6.0f, s_i = a / 7.0f;
+    const float r_f = (a > 0.0f) ? 1.0f / s_f : 0.0f;
+    const float r_i = (a > 0.0f) ? 1.0f / s_i : 0.0f;
+    int mf[16], mi[16];
+    float hf[16], hi[16], sqf[16], sqi[16];
+    for (int i = 0; i < 16; i++) {
+      mf[i] = (a > 0.0f) ? orc_e2m1_rne(fminf(fabsf(zb[i] * r_f), 6.0f)) : 0;
+      mi[i] = (a > 0.0f) ? orc_int4_rne(fminf(fabsf(zb[i] * r_i), 7.0f)) : 0;
+      float vf = signbit(zb[i]) ? -GRID_E2M1[mf[i]] : GRID_E2M1[mf[i]];
+      float vi = signbit(zb[i]) ? -(float)mi[i] : (float)mi[i];
+      hf[i] = vf * s_f;
+      hi[i] = vi * s_i;
+      float df = zb[i] - hf[i], di = zb[i] - hi[i];
+      sqf[i] = df * df;
+      sqi[i] = di * di;
+    }
+    const int use_int = orc_pairwise_sum(sqi, 16) < orc_pairwise_sum(sqf, 16);
+    flag[b] = (uint8_t)use_int;
+    s_b[b] = use_int ? s_i : s_f;
+    for (int i = 0; i < 16; i++) {
+      zh[16 * b + i] = use_int ? hi[i] : hf[i];
+      put_nibble(codes_row, k0 + 16 * b + i, (signbit(zb[i]) ? 8 : 0) | (use_int ? mi[i] : mf[i]));
+    }
+  }
+  for (int i = 0; i < G; i++) {
+    zz[i] = z[i] * z[i];
+    zh[i] = z[i] * zh[i];
+  }
+  float N = orc_pairwise_sum(zz, G);
+  float D = orc_pairwise_sum(zh, G);
+  float c = (D > 0.0f) ? N / D : 1.0f;
+  for (int b = 0; b < G / 16; b++) tb[b] = s_b[b] * c;
+}
+
 /* View the input as the [rows_out x K] matrix whose rows are quantization
  * groups: axis 0 keeps rows (groups run along the contiguous dimension);
  * axis 1 transposes (groups run along the strided dimension, i.e. along the
@@ -526,7 +649,7 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
   if (!x || !codes || !scales || !ts_out) return ORC_BAD_ARG;
   if (format < 0 || format > 4 || rounding < 0 || rounding > 2 || axis < 0 || axis > 1)
     return ORC_BAD_ARG;
-  if (format != ORC_FMT_NVFP4 && rounding != ORC_RTN) return ORC_BAD_ARG;
+  if (format != ORC_FMT_NVFP4 && format != ORC_FMT_IF4 && rounding != ORC_RTN) return ORC_BAD_ARG;
   if (rows < 0 || cols < 0 || ld < cols) return ORC_BAD_SHAPE;
   const int64_t R = axis == 0 ? rows : cols;
   const int64_t K = axis == 0 ? cols : rows;
@@ -581,6 +704,8 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
         if (format == ORC_FMT_NVFP4)
           nvfp4_block(zb, s_t, rounding, seed, stream, (uint64_t)(r * K + k), codes + r * (K / 2),
                       k, sc);
+        else if (format == ORC_FMT_IF4 && rounding == ORC_SR)
+          if4_sr_block(zb, s_t, seed, stream, (uint64_t)(r * K + k), codes + r * (K / 2), k, sc);
         else if (format == ORC_FMT_NVFP4_4OVER6)
           fos_block(zb, s_t, codes + r * (K / 2), k, sc);
         else if (format == ORC_FMT_NVFP4_SEARCH)
@@ -592,11 +717,17 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
     /* MS-EDEN: codes and target scales t_b per group, then the tensor scale
      * from the largest target, then the E4M3 scales by SR of t_b / s_t. */
     float *tb = (float *)malloc(sizeof(float) * (size_t)(R * K / 16));
-    if (!tb) { free(Z); return ORC_BAD_ARG; }
+    uint8_t *flag = (uint8_t *)calloc((size_t)(R * K / 16), 1);
+    if (!tb || !flag) { free(tb); free(flag); free(Z); return ORC_BAD_ARG; }
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < R; r++)
-      for (int64_t k = 0; k < K; k += G)
-        eden_group(Z + r * K + k, G, codes + r * (K / 2), k, tb + r * (K / 16) + k / 16);
+      for (int64_t k = 0; k < K; k += G) {
+        if (format == ORC_FMT_IF4)
+          eden_group_if4(Z + r * K + k, G, codes + r * (K / 2), k, tb + r * (K / 16) + k / 16,
+                         flag + r * (K / 16) + k / 16);
+        else
+          eden_group(Z + r * K + k, G, codes + r * (K / 2), k, tb + r * (K / 16) + k / 16);
+      }
     float s_t;
     if (ts_in) {
       s_t = *ts_in;
@@ -613,10 +744,12 @@ int orc_quantize(const float *x, int64_t rows, int64_t cols, int64_t ld,
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < R * K / 16; b++) {
       float a = fminf(tb[b] / s_t, 448.0f);
-      scales[b] = (uint8_t)orc_sr_e4m3(a, orc_uniform16(seed, 1, stream, (uint64_t)b));
+      scales[b] = (uint8_t)(orc_sr_e4m3(a, orc_uniform16(seed, 1, stream, (uint64_t)b)) |
+                            (flag[b] ? 0x80 : 0));
     }
     if (tb_out) memcpy(tb_out, tb, sizeof(float) * (size_t)(R * K / 16));
     free(tb);
+    free(flag);
   }
   free(Z);
   return ORC_OK;

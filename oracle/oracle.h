@@ -39,6 +39,7 @@ int orc_e2m1_rne(float a);                 /* 0 <= a <= 6 -> magnitude 0..7   */
 int orc_int4_rne(float a);                 /* 0 <= a <= 7 -> 0..7             */
 int orc_sr_e2m1(float a, uint32_t u16);    /* 0 <= a <= 6 -> magnitude 0..7   */
 int orc_sr_e4m3(float a, uint32_t u16);    /* 0 <= a <= 448 -> byte           */
+float orc_sr_expected_sq(float a, int is_int); /* (a-l)(u-a) on E2M1 / 0..7 */
 
 /* the rules above over consecutive fp32 bit patterns (exhaustive checks) */
 void orc_e2m1_rne_run(uint32_t bits_lo, uint64_t count, uint8_t *codes);
