@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -214,11 +214,25 @@ size_t nvfp4_workspace_size_dual(int64_t rows, int64_t cols, const nvfp4_opts *o
 
 /*
  * IF4 quantization [IF4 abstract, Figure 1, Figure 3]: every 16-group is
- * quantized as NVFP4 (E2M1 under scale a/6) and as scaled INT4 (integers
- * 0..7 under its own scale a/7, both RNE), and keeps the one with the
- * smaller sum of squared errors (ties keep FP4); the INT choice sets bit 7
- * of the scale byte.  Tensor scale s_t = max|z| / (6 * 448).  Same arguments
- * and layout rules as nvfp4_quantize_nvfp4; o->rounding must be NVFP4_RTN.
+ * coded two ways, as NVFP4 (E2M1 levels) and as scaled INT4 (integers 0..7),
+ * and keeps the better one; the INT choice sets bit 7 of the scale byte.
+ * Same arguments, options and layout rules as nvfp4_quantize_nvfp4 (scale
+ * rule MAX6 only); o->rounding selects how:
+ *   RTN: E2M1 under the RNE scale of a/6, integers under the RNE scale of
+ *     a/7 (both RNE), keep the smaller pairwise sum of squared errors (ties
+ *     keep FP4); s_t = max|z| / (6 * 448).
+ *   SR (gradients; IF4 Figure 4): both branches as NVFP4 SR, scales rounded
+ *     up from a/6 and from a/7, elements rounded stochastically (Philox tag
+ *     0, the element's uniform whichever branch is kept); the branch is
+ *     chosen before rounding, by the smaller expected squared error
+ *     (S*S) * sum (y - l)(u - y) [PAL opening paragraph], ties FP4;
+ *     s_t = max|z| / (6 * 448).
+ *   MSEDEN (gradients; IF4 Figure 4 with QII-abs): RTN codes in both branches
+ *     under the exact scales a/6 and a/7, keep the smaller pairwise squared
+ *     error (ties FP4); the correction c = sum z^2 / sum z*zhat over the
+ *     correction group uses the kept reconstructions; target t = (kept
+ *     exact scale) * c, s_t = max t / 448, scale = SR of t/s_t onto E4M3
+ *     (Philox tag 1) with the flag in bit 7.  amax_out as for NVFP4 MS-EDEN.
  */
 int nvfp4_quantize_if4(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
                        const nvfp4_opts *o, uint8_t *codes, uint8_t *scales,

@@ -347,10 +347,15 @@ def workspace_size_dual(rows, cols, eden_group=128, tensor_scale_in=None):
     return int(lib().nvfp4_workspace_size_dual(int(rows), int(cols), ctypes.byref(o)))
 
 
-def quantize_if4(x, axis=0, rht_signs=None, tensor_scale_in=None, out=None, workspace=None, amax_in=None):
-    """IF4 quantization (per-16 FP4/INT4 choice by lower squared error)."""
-    return _quantize(lib().nvfp4_quantize_if4, x, RTN, axis, rht_signs, 0, 0, 128, tensor_scale_in,
-                     out, workspace, FORMAT_IF4, amax_in=amax_in)
+def quantize_if4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0, eden_group=128,
+                 tensor_scale_in=None, out=None, workspace=None, amax_out=None, amax_in=None):
+    """IF4 quantization (per-16 FP4/INT4 choice): RTN keeps the branch with
+    the lower squared error; SR the one with the lower expected error of
+    stochastic rounding; MS-EDEN codes both by RTN under exact scales, keeps
+    the better and folds the EDEN correction into the stochastic scale (see
+    ``nvfp4_quantize_if4``).  Returns a QTensor of format FORMAT_IF4."""
+    return _quantize(lib().nvfp4_quantize_if4, x, rounding, axis, rht_signs, seed, stream_id, eden_group,
+                     tensor_scale_in, out, workspace, FORMAT_IF4, amax_out=amax_out, amax_in=amax_in)
 
 
 def dequantize(q, inv_rht_signs=None, out_dtype=None, out=None):

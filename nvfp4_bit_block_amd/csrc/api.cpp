@@ -57,8 +57,6 @@ int check_input(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t
     return fail(NVFP4_INVALID_ARG, "in_dtype %d is not NVFP4_F32 or NVFP4_BF16", in_dtype);
   if (o->rounding < NVFP4_RTN || o->rounding > NVFP4_MSEDEN)
     return fail(NVFP4_INVALID_ARG, "rounding %d is not RTN, SR or MSEDEN", o->rounding);
-  if (if4 && o->rounding != NVFP4_RTN)
-    return fail(NVFP4_INVALID_ARG, "IF4 quantization takes rounding RTN only");
   if (o->axis != 0 && o->axis != 1) return fail(NVFP4_INVALID_ARG, "axis %d is not 0 or 1", o->axis);
   if (o->rht != 0 && o->rht != 1) return fail(NVFP4_INVALID_ARG, "rht %d is not 0 or 1", o->rht);
   if (o->scale_rule != NVFP4_SCALE_MAX6 && o->scale_rule != NVFP4_SCALE_4OVER6 &&
@@ -199,16 +197,16 @@ int quantize_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, int64
   hipError_t e = hipSuccess;
   if (o->rounding == NVFP4_MSEDEN) {
     if (o->tensor_scale_in) {
-      e = launch_quant(p, bf, o->axis, kEdenFused, grid, s);
+      e = launch_quant(p, bf, o->axis, if4 ? kIf4EdenFused : kEdenFused, grid, s);
     } else {
-      e = launch_quant(p, bf, o->axis, kEden, grid, s);
+      e = launch_quant(p, bf, o->axis, if4 ? kIf4Eden : kEden, grid, s);
       if (e == hipSuccess) {
         p.npartial = grid;
         e = launch_eden_scales(p, eden_scales_grid(p), s);
       }
     }
   } else {
-    const Mode m = if4 ? kIf4
+    const Mode m = if4 ? (o->rounding == NVFP4_SR ? kIf4Sr : kIf4)
                    : o->rounding == NVFP4_SR ? kSr
                    : o->scale_rule == NVFP4_SCALE_4OVER6 ? kFos
                    : o->scale_rule == NVFP4_SCALE_SEARCH ? kSearch

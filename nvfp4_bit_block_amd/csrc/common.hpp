@@ -152,6 +152,33 @@ __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t u16) {
   return (uint32_t)(2 * E + (int)f + up);
 }
 
+// Stochastic rounding onto the integers 0..7 (IF4's INT branch): up iff
+// u16 < frac * 65536, frac = a - floor(a) (exact); 7 and above give 7.
+__device__ __forceinline__ uint32_t int4_sr(float a, uint32_t u16) {
+  if (a >= 7.0f) return 7u;
+  const float f = floorf(a);
+  const float p = a - f;
+  return (uint32_t)f + (((float)u16 < p * 65536.0f) ? 1u : 0u);
+}
+
+// Expected squared error of stochastic rounding, in grid units: (a - l)(u - a)
+// with l <= a < u the neighbouring levels; 0 at the top level.  On the E2M1
+// grid l = f * 2^(E-1), u = (f + 1) * 2^(E-1) (both exact) with E and f as in
+// e2m1_sr; on the integers l = floor(a), u = l + 1.
+__device__ __forceinline__ float e2m1_sr_err(float a) {
+  const int E = ilog2_floor_clamped(a, 0);
+  const float g = pow2i(E - 1);
+  const float f = floorf(a * pow2i(1 - E));
+  const float d = (a - f * g) * ((f + 1.0f) * g - a);
+  return a >= 6.0f ? 0.0f : d;
+}
+
+__device__ __forceinline__ float int4_sr_err(float a) {
+  const float f = floorf(a);
+  const float d = (a - f) * ((f + 1.0f) - a);
+  return a >= 7.0f ? 0.0f : d;
+}
+
 // Value of a magnitude code 0..7.
 __device__ __forceinline__ float e2m1_value(uint32_t mag) {
   return (mag < 2u) ? 0.5f * (float)mag : (float)(2u + (mag & 1u)) * pow2i((int)(mag >> 1) - 2);

@@ -18,8 +18,19 @@ enum Mode : int {
   kEdenFused = 5,  // MS-EDEN with a given tensor scale: codes + scales in one pass
   kRot = 6,        // rotation only: rotated fp32 values
   kFos = 7,        // NVFP4 RTN, Four Over Six block scale (maximum -> 6 or 4)
-  kSearch = 8      // NVFP4 RTN, block scale searched over 19 E4M3 bytes
+  kSearch = 8,     // NVFP4 RTN, block scale searched over 19 E4M3 bytes
+  kIf4Sr = 9,      // IF4 with stochastic rounding (branch by expected error)
+  kIf4Eden = 10,   // IF4 MS-EDEN pass 1: codes + flagged target scales + partials
+  kIf4EdenFused = 11  // IF4 MS-EDEN with a given tensor scale
 };
+
+// Passes that code with a known tensor scale, and passes that end with
+// per-workgroup partial maxima for the next pass.
+constexpr bool takes_tensor_scale(int m) {
+  return m == kRtn || m == kSr || m == kIf4 || m == kFos || m == kSearch || m == kEdenFused || m == kIf4Sr ||
+         m == kIf4EdenFused;
+}
+constexpr bool writes_partials(int m) { return m == kAmax || m == kEden || m == kIf4Eden; }
 
 constexpr int kThreads = 256;      // threads per workgroup of every quantizer
 constexpr int kMaxPartials = 2048; // workgroups of a pass that writes partials
@@ -45,7 +56,7 @@ struct QuantParams {
   float *ts_out;
   float *partial;       // kMaxPartials floats of workspace
   uint32_t npartial;    // partial maxima written by the previous pass
-  float *tb;            // MS-EDEN target scales, nblocks floats of workspace
+  float *tb;            // MS-EDEN target scales, nblocks floats of workspace (IF4: sign bit = INT flag)
   const float *ts_in;   // given tensor scale or nullptr
   const float *amax_in; // given max|x| (tensor scale amax_in / top) or nullptr
   float *amax_out;      // MS-EDEN: max|x| of the raw input written here, or nullptr

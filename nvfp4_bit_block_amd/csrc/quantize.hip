@@ -247,6 +247,39 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       const bool use_int = tree16(sqi) < tree16(sqf);
       out.codes(use_int ? ilo : flo, use_int ? ihi : fhi);
       out.scale(use_int ? (ei | 0x80u) : ef);
+    } else if constexpr (MODE == kIf4Sr) {
+      // both branches as NVFP4 SR: scales rounded up from a/6 (E2M1) and
+      // a/7 (integers); keep the smaller closed-form expected squared error
+      // (S*S) * sum (y - l)(u - y), decided before any random draw; the
+      // kept branch rounds with the element's uniform.
+      const uint32_t ef = e4m3_ceil_sat(div_rn(div_by<6>(a), s_t));
+      const float Sf = e4m3_value(ef) * s_t;
+      const float rf = ef ? rcp_rn(Sf) : 0.0f;
+      const uint32_t ei = e4m3_ceil_sat(div_rn(div_by<7>(a), s_t));
+      const float Si = e4m3_value(ei) * s_t;
+      const float ri = ei ? rcp_rn(Si) : 0.0f;
+      float yf[16], yi[16], df[16], di[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        yf[i] = ef ? fminf(fabsf(z[i] * rf), 6.0f) : 0.0f;
+        yi[i] = ei ? fminf(fabsf(z[i] * ri), 7.0f) : 0.0f;
+        df[i] = e2m1_sr_err(yf[i]);
+        di[i] = int4_sr_err(yi[i]);
+      }
+      const bool use_int = (Si * Si) * tree16(di) < (Sf * Sf) * tree16(df);
+      const Philox4 u0 = uniforms8(p.key, (uint64_t)gb * 2u, 0u);
+      const Philox4 u1 = uniforms8(p.key, (uint64_t)gb * 2u + 1u, 0u);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t u = uniform_at(i < 8 ? u0 : u1, i & 7);
+        const uint32_t mag = use_int ? (ei ? int4_sr(yi[i], u) : 0u) : (ef ? e2m1_sr(yf[i], u) : 0u);
+        const uint32_t nib = sign_nib(z[i]) | mag;
+        if (i < 8) lo |= nib << (4 * i);
+        else hi |= nib << (4 * (i - 8));
+      }
+      out.codes(lo, hi);
+      out.scale(use_int ? (ei | 0x80u) : ef);
     } else if constexpr (MODE == kFos) {
       // Four Over Six: RTN with the block maximum mapped to 6 and to 4;
       // keep the smaller pairwise SSE (tie: 6).
@@ -311,10 +344,13 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       }
       out.codes(blo, bhi);
       out.scale(best_e);
-    } else if constexpr (MODE == kEden || MODE == kEdenFused) {
-      // RTN codes under the exact scale a/6; correction c = sum z^2 /
-      // sum z*zhat over the group; target t = (a/6) * c.
-      const float s_b = div_by<6>(a);
+    } else if constexpr (MODE == kEden || MODE == kEdenFused || MODE == kIf4Eden || MODE == kIf4EdenFused) {
+      // RTN codes under the exact scale a/6 (IF4: also integers under a/7,
+      // keeping the branch with the smaller pairwise squared error);
+      // correction c = sum z^2 / sum z*zhat over the group; target
+      // t = (kept exact scale) * c.
+      constexpr bool IF4 = MODE == kIf4Eden || MODE == kIf4EdenFused;
+      float s_b = div_by<6>(a);
       const float r = (a > 0.0f) ? rcp_rn(s_b) : 0.0f;
       float nn[16], dd[16], y[16], g[16];
       uint32_t lo, hi;
@@ -322,6 +358,33 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       for (int i = 0; i < 16; ++i) y[i] = z[i] * r;  // r = 0 when a = 0: signed zeros
       e2m1x16_rne(y, lo, hi);
       e2m1x16_value(lo, hi, g);  // signed grid values
+      bool use_int = false;
+      if constexpr (IF4) {
+        const float si = div_by<7>(a);
+        const float ri = (a > 0.0f) ? rcp_rn(si) : 0.0f;
+        float sqf[16], sqi[16], gi[16];
+        uint32_t ilo = 0, ihi = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float df = z[i] - g[i] * s_b;
+          sqf[i] = df * df;
+          const uint32_t sn = sign_nib(z[i]);
+          const uint32_t mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
+          gi[i] = sn ? -(float)mi : (float)mi;
+          const float di = z[i] - gi[i] * si;
+          sqi[i] = di * di;
+          if (i < 8) ilo |= (sn | mi) << (4 * i);
+          else ihi |= (sn | mi) << (4 * (i - 8));
+        }
+        use_int = tree16(sqi) < tree16(sqf);
+        if (use_int) {
+          lo = ilo;
+          hi = ihi;
+          s_b = si;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) g[i] = gi[i];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float zh = g[i] * s_b;
@@ -339,15 +402,15 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       }
       const float c = (D > 0.0f) ? div_rn(N, D) : 1.0f;
       const float t = s_b * c;
-      if constexpr (MODE == kEden) {
+      if constexpr (MODE == kEden || MODE == kIf4Eden) {
         out.codes(lo, hi);
-        out.target(t);
+        out.target(use_int ? -t : t);  // t >= +0: the sign bit carries the INT flag
         if (active) lmax = fmaxf(lmax, t);
       } else {
         const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);
         const uint32_t e = e4m3_sr_sat(fminf(div_rn(t, s_t), 448.0f), uniform_at(u, (int)(gb & 7u)));
         out.codes(lo, hi);
-        out.scale(e);
+        out.scale(use_int ? (e | 0x80u) : e);
       }
     }
   }
@@ -414,8 +477,7 @@ template <int IN_BF16, int MODE, int RAW = 0>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
-  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kSearch ||
-                MODE == kEdenFused) {
+  if constexpr (takes_tensor_scale(MODE)) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
@@ -454,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
     else quant_block<MODE>(z, gb, RowSink(p, base, rank), p, s_t, lmax);
     cur = nxt;
   }
-  if constexpr (MODE == kAmax || MODE == kEden) {
+  if constexpr (writes_partials(MODE)) {
     const float m = block_max(lmax, red, kThreads);
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
   }
@@ -593,8 +655,7 @@ template <int IN_BF16, int MODE, int RAW = 0>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t = 1.0f;
-  if constexpr (MODE == kRtn || MODE == kSr || MODE == kIf4 || MODE == kFos || MODE == kSearch ||
-                MODE == kEdenFused) {
+  if constexpr (takes_tensor_scale(MODE)) {
     s_t = tensor_scale(p, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
   }
@@ -611,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantParams p) {
     const uint32_t tc = t - tt * nct;
     col_tile<IN_BF16, MODE, RAW>(p, tt, tc, lig, q, sbits, s_t, lmax, araw);
   }
-  if constexpr (MODE == kAmax || MODE == kEden) {
+  if constexpr (writes_partials(MODE)) {
     const float m = block_max(lmax, red, kThreads);
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
   }
@@ -677,6 +738,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
 }
 
 // ---------------------------------------------------------------- MS-EDEN scales
+// Scale byte of a target t (sign bit: IF4's INT flag, bit 7 of the byte).
+__device__ __forceinline__ uint32_t eden_scale_byte(float t, float s_t, uint32_t u16) {
+  const uint32_t flag = (__float_as_uint(t) >> 24) & 0x80u;
+  return e4m3_sr_sat(fminf(div_rn(fabsf(t), s_t), 448.0f), u16) | flag;
+}
+
 // s_t = max t / 448 (or the given scale); scale = SR of min(t / s_t, 448)
 // onto the E4M3 grid, one Philox call per 8 consecutive blocks (tag 1).
 __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
@@ -703,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t e = e4m3_sr_sat(fminf(div_rn(t[j], s_t), 448.0f), uniform_at(u, j));
+      const uint32_t e = eden_scale_byte(t[j], s_t, uniform_at(u, j));
       if (j < 4) lo |= e << (8 * j);
       else hi |= e << (8 * (j - 4));
     }
@@ -725,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
   if (p.nblocks % 8u && blockIdx.x * kThreads + threadIdx.x == nfull % stride) {
     const Philox4 u = uniforms8(p.key, (uint64_t)nfull, 1u);
     for (uint32_t j = 0; nfull * 8u + j < p.nblocks; ++j)
-      p.scales[nfull * 8u + j] = (uint8_t)e4m3_sr_sat(fminf(div_rn(p.tb[nfull * 8u + j], s_t), 448.0f), uniform_at(u, (int)j));
+      p.scales[nfull * 8u + j] = (uint8_t)eden_scale_byte(p.tb[nfull * 8u + j], s_t, uniform_at(u, (int)j));
   }
 }
 
@@ -775,6 +842,18 @@ static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid
     case kRot: launch_one<IN_BF16, kRot>(p, axis, grid, s); break;
     case kFos: launch_one<IN_BF16, kFos>(p, axis, grid, s); break;
     case kSearch: launch_one<IN_BF16, kSearch>(p, axis, grid, s); break;
+    case kIf4Sr: launch_one<IN_BF16, kIf4Sr>(p, axis, grid, s); break;
+    case kIf4Eden:
+      if (p.amax_out) {
+        if (axis == 0)
+          hipLaunchKernelGGL((k_quant_rows<IN_BF16, kIf4Eden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
+        else
+          hipLaunchKernelGGL((k_quant_cols<IN_BF16, kIf4Eden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
+      } else {
+        launch_one<IN_BF16, kIf4Eden>(p, axis, grid, s);
+      }
+      break;
+    case kIf4EdenFused: launch_one<IN_BF16, kIf4EdenFused>(p, axis, grid, s); break;
   }
 }
 

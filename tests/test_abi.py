@@ -42,7 +42,7 @@ def test_header_functions_exported(nv):
 
 def test_version_and_strings(nv):
     L = nv.lib()
-    assert nv.abi_version() == 4
+    assert nv.abi_version() == 5
     for st, text in ((OK, b"ok"), (INVALID, b"invalid argument"), (SHAPE, b"bad shape"),
                      (MISALIGNED, b"misaligned pointer or stride"), (WS_SMALL, b"workspace too small"),
                      (HIP_ERR, b"HIP error"), (UNSUPPORTED, b"unsupported")):
@@ -105,7 +105,12 @@ def test_quantize_rejections(nv):
     assert _q(nv, codes=FAKE + 4) == MISALIGNED
     assert _q(nv, ws=FAKE + 16) == MISALIGNED
     assert _q(nv, ws_bytes=100) == WS_SMALL
-    assert _q(nv, fn="nvfp4_quantize_if4", rounding=1) == INVALID
+    # IF4 takes all three roundings (SR and MS-EDEN for gradients); the MS-EDEN
+    # workspace holds the target scales, so a small one is rejected
+    assert _q(nv, fn="nvfp4_quantize_if4", rounding=1, ws_bytes=100) == WS_SMALL   # accepted (fails later)
+    assert _q(nv, fn="nvfp4_quantize_if4", rounding=2, ws_bytes=16384) == WS_SMALL
+    assert _q(nv, fn="nvfp4_quantize_if4", rounding=3) == INVALID
+    assert _q(nv, fn="nvfp4_quantize_if4", rounding=2, amax_out=FAKE, ws_bytes=100) == WS_SMALL
     assert _q(nv, scale_rule=3) == INVALID
     assert _q(nv, scale_rule=2, rounding=1) == INVALID        # scale search: RTN only
     assert _q(nv, scale_rule=1, rounding=1) == INVALID        # Four Over Six: RTN only
