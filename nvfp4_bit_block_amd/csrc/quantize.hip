@@ -404,7 +404,9 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       const float t = s_b * c;
       if constexpr (MODE == kEden || MODE == kIf4Eden) {
         out.codes(lo, hi);
-        out.target(use_int ? -t : t);  // t >= +0: the sign bit carries the INT flag
+        // the sign bit carries the INT flag (t >= +0, or NaN where the group's
+        // sums overflow, whose sign is the division's)
+        out.target(use_int ? -fabsf(t) : fabsf(t));
         if (active) lmax = fmaxf(lmax, t);
       } else {
         const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);

@@ -22,6 +22,13 @@ MODES = [  # (name, oracle format, oracle rounding, binding kwargs)
     ("4over6", oracle.FMT_NVFP4_4OVER6, oracle.RTN, dict(scale_rule="4over6")),
     ("search", oracle.FMT_NVFP4_SEARCH, oracle.RTN, dict(scale_rule="search")),
 ]
+# IF4 for gradients (swept on cases of their own, so that the cases above
+# keep their draws)
+MODES_IF4_GRAD = [
+    ("if4_sr", oracle.FMT_IF4, oracle.SR, dict(rounding="sr", if4=True)),
+    ("if4_mseden128", oracle.FMT_IF4, oracle.MSEDEN, dict(rounding="mseden", eden_group=128, if4=True)),
+    ("if4_mseden16", oracle.FMT_IF4, oracle.MSEDEN, dict(rounding="mseden", eden_group=16, if4=True)),
+]
 
 
 def _values(rng, rows, cols, kind, dtype):
@@ -40,13 +47,13 @@ def _values(rng, rows, cols, kind, dtype):
     return synth.to_bf16_f32(x) if dtype == "bf16" else x
 
 
-def _case(i):
-    rng = np.random.default_rng([2026, i])
-    name, fmt, rnd, kw = MODES[i % len(MODES)]
+def _case(i, modes=MODES, base=2026):
+    rng = np.random.default_rng([base, i])
+    name, fmt, rnd, kw = modes[i % len(modes)]
     dtype = ("bf16", "fp32")[rng.integers(0, 2)]
     axis = int(rng.integers(0, 2))
     rot = bool(rng.integers(0, 2))
-    need128 = rot or name == "mseden128"
+    need128 = rot or name.endswith("mseden128")
     k_unit = 128 if need128 else 16
     K = int(rng.integers(1, 5 if need128 else 24)) * k_unit
     R = int(rng.integers(1, 200))
@@ -78,6 +85,10 @@ def _run(nv, c):
     tsd = None if ts is None else torch.tensor([ts], device="cuda:0")
     if c["kw"] is None:
         q = nv.quantize_if4(x, axis=c["axis"], rht_signs=c["signs"], tensor_scale_in=tsd)
+    elif c["kw"].get("if4"):
+        kw = {k: v for k, v in c["kw"].items() if k != "if4"}
+        q = nv.quantize_if4(x, axis=c["axis"], rht_signs=c["signs"], seed=c["seed"], stream_id=c["stream"],
+                            tensor_scale_in=tsd, **kw)
     else:
         q = nv.quantize_nvfp4(x, axis=c["axis"], rht_signs=c["signs"], seed=c["seed"], stream_id=c["stream"],
                               tensor_scale_in=tsd, **c["kw"])
@@ -94,6 +105,19 @@ def test_quantize_sweep(nv, i):
     c = _case(i)
     q, ref = _run(nv, c)
     what = (f"case {i}: {c['name']} {c['dtype']} axis{c['axis']} {c['x'].shape} rot={c['rot']} "
+            f"{c['kind']} given_ts={c['given']}")
+    g = q_to_host(q)
+    if c["rot"]:
+        assert_rotated_close(g, ref, what=what)
+    else:
+        assert_bit_exact(g, ref, what)
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_if4_gradient_sweep(nv, i):
+    c = _case(i, MODES_IF4_GRAD, 2028)
+    q, ref = _run(nv, c)
+    what = (f"IF4 gradient case {i}: {c['name']} {c['dtype']} axis{c['axis']} {c['x'].shape} rot={c['rot']} "
             f"{c['kind']} given_ts={c['given']}")
     g = q_to_host(q)
     if c["rot"]:
