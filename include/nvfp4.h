@@ -209,6 +209,26 @@ int nvfp4_quantize_nvfp4_dual(const void *x, int in_dtype, int64_t rows, int64_t
                               uint8_t *codes_c, uint8_t *scales_c, float *ts_c, void *ws,
                               size_t ws_bytes, void *stream);
 
+/*
+ * nvfp4_quantize_nvfp4 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The library's own scratch array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES per GPU (reserved when the library's device
+ * code is loaded on that GPU, and held until the process ends) stands in for
+ * the workspace; the call itself allocates nothing.  Results, arguments and
+ * errors are those of nvfp4_quantize_nvfp4; a call whose
+ * nvfp4_workspace_size() exceeds the scratch (MS-EDEN with a computed tensor
+ * scale on more than 24 * 2^20 blocks, about 403 M elements) returns
+ * NVFP4_UNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (on different
+ * streams, or from several host threads) race and give unspecified results;
+ * calls ordered on one stream do not.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)16384 + ((size_t)96 << 20))
+int nvfp4_quantize_nvfp4_noalloc(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                 const nvfp4_opts *o, uint8_t *codes, uint8_t *scales,
+                                 float *tensor_scale, void *stream);
+
 /* Workspace bytes of nvfp4_quantize_nvfp4_dual (both axes' workspaces). */
 size_t nvfp4_workspace_size_dual(int64_t rows, int64_t cols, const nvfp4_opts *o);
 

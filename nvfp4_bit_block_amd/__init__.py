@@ -18,7 +18,7 @@ __all__ = [
     "RTN", "SR", "MSEDEN", "FORMAT_NVFP4", "FORMAT_IF4", "QTensor", "NvFp4Error",
     "lib", "signs_to_words", "workspace_size", "quantize_nvfp4", "quantize_if4",
     "dequantize", "gemm_nvfp4", "rht", "abi_version", "SCALE_MAX6", "SCALE_4OVER6", "SCALE_SEARCH",
-    "quantize_nvfp4_dual", "workspace_size_dual", "gemm_nvfp4_rtn",
+    "quantize_nvfp4_dual", "workspace_size_dual", "gemm_nvfp4_rtn", "quantize_nvfp4_noalloc",
 ]
 
 RTN, SR, MSEDEN = 0, 1, 2
@@ -81,6 +81,8 @@ def lib():
         f = getattr(L, name)
         f.restype = INT
         f.argtypes = [P, INT, I64, I64, I64, ctypes.POINTER(_Opts), P, P, P, P, SZ, P]
+    L.nvfp4_quantize_nvfp4_noalloc.restype = INT
+    L.nvfp4_quantize_nvfp4_noalloc.argtypes = [P, INT, I64, I64, I64, ctypes.POINTER(_Opts), P, P, P, P]
     L.nvfp4_dequantize.restype = INT
     L.nvfp4_dequantize.argtypes = [P, P, P, I64, I64, INT, P, INT, P, P]
     for name in ("nvfp4_gemm_nvfp4", "nvfp4_gemm_if4"):
@@ -300,6 +302,34 @@ def quantize_nvfp4(x, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0,
     return _quantize(lib().nvfp4_quantize_nvfp4, x, rounding, axis, rht_signs, seed, stream_id,
                      eden_group, tensor_scale_in, out, workspace, FORMAT_NVFP4, scale_rule,
                      amax_out, amax_in)
+
+
+def quantize_nvfp4_noalloc(x, out, rounding=RTN, axis=0, rht_signs=None, seed=0, stream_id=0, eden_group=128,
+                           tensor_scale_in=None, scale_rule=SCALE_MAX6, amax_out=None, amax_in=None):
+    """quantize_nvfp4 through ``nvfp4_quantize_nvfp4_noalloc``: no workspace,
+    the library's per-GPU scratch instead, and nothing allocated -- so the
+    caller passes the output QTensor `out` (codes [R, K/2], scales [R, K/16],
+    tensor scale [1]).  Calls that overlap on one GPU race on that scratch."""
+    L = lib()
+    _check_input(x)
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else cols
+    dev = x.device
+    for t, n in ((amax_out, "amax_out"), (amax_in, "amax_in"), (tensor_scale_in, "tensor_scale_in")):
+        _check_scalar(t, n, dev)
+    R, K = (rows, cols) if axis == 0 else (cols, rows)
+    if K % 16 == 0:
+        _check_qtensor(out, "out", rows=R, k=K, dev=dev)
+    o = _opts(rounding, axis, rht_signs, seed, stream_id, eden_group, tensor_scale_in, scale_rule, amax_out,
+              amax_in)
+    import torch
+    rc = L.nvfp4_quantize_nvfp4_noalloc(ctypes.c_void_p(x.data_ptr()), _dtype_code(x, torch), rows, cols, ld,
+                                        ctypes.byref(o), ctypes.c_void_p(out.codes.data_ptr()),
+                                        ctypes.c_void_p(out.scales.data_ptr()),
+                                        ctypes.c_void_p(out.tensor_scale.data_ptr()), _stream(torch))
+    _check(rc)
+    out.format = FORMAT_NVFP4
+    return out
 
 
 def quantize_nvfp4_dual(x, rht_signs=None, seed=0, stream_id=0, eden_group=128, tensor_scale_in=None,

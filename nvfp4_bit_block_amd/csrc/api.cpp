@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/nvfp4.h"
@@ -166,17 +167,7 @@ void fill_common(QuantParams &p, const void *x, int in_dtype, int64_t rows, int6
 // Zero-size tensor: only the tensor scale is defined (the given one, or 1),
 // and the maximum (0) if it is asked for.
 int write_trivial_scale(const nvfp4_opts *o, float *tensor_scale, hipStream_t s) {
-  hipError_t e;
-  if (o->tensor_scale_in)
-    e = hipMemcpyAsync(tensor_scale, o->tensor_scale_in, sizeof(float), hipMemcpyDeviceToDevice, s);
-  else {
-    static const float one = 1.0f;
-    e = hipMemcpyAsync(tensor_scale, &one, sizeof(float), hipMemcpyHostToDevice, s);
-  }
-  if (e == hipSuccess && o->amax_out) {
-    static const float zero = 0.0f;
-    e = hipMemcpyAsync(o->amax_out, &zero, sizeof(float), hipMemcpyHostToDevice, s);
-  }
+  const hipError_t e = launch_trivial_scale(tensor_scale, o->tensor_scale_in, o->amax_out, s);
   if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "%s", hipGetErrorString(e));
   return ok();
 }
@@ -475,6 +466,61 @@ int nvfp4_rht(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t l
   hipError_t e = launch_quant(p, bf, axis, kRot, quant_grid(p, bf, axis), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free entry point
+// The workspace of nvfp4_quantize_nvfp4_noalloc: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is a stand-in, not device
+// memory): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address reaches kernels.
+constexpr size_t kScratchBytes = NVFP4_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0 && kScratchBytes > kPartialBytes, "scratch layout");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// This device's copy of the scratch array (looked up on its first use).
+int device_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(NVFP4_UNSUPPORTED, "device %d above the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(NVFP4_HIP_ERROR, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize_nvfp4_noalloc(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                 const nvfp4_opts *o, uint8_t *codes, uint8_t *scales, float *tensor_scale,
+                                 void *stream) {
+  if (!o) return fail(NVFP4_INVALID_ARG, "opts is NULL");
+  if (rows < 0 || cols < 0) return fail(NVFP4_INVALID_ARG, "negative shape");
+  const size_t need = nvfp4_workspace_size(rows, cols, o);
+  if (need > kScratchBytes)
+    return fail(NVFP4_UNSUPPORTED, "this call needs %zu bytes of workspace, above the %zu bytes of the "
+                "allocation-free entry point's scratch (use nvfp4_quantize_nvfp4 with a workspace)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  const int st = device_scratch(&ws);
+  if (st) return st;
+  return quantize_impl(x, in_dtype, rows, cols, ld, o, codes, scales, tensor_scale, ws, kScratchBytes, stream,
+                       false);
 }
 
 const char *nvfp4_status_string(int status) {

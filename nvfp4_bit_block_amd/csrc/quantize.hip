@@ -887,6 +887,18 @@ hipError_t launch_quant_dual(const QuantParams &pr, const QuantParams &pc, int i
   return hipGetLastError();
 }
 
+// Empty tensor: the tensor scale is the given one or 1, the maximum 0 (a
+// kernel rather than copies, so that nothing is staged through host memory).
+__global__ void k_trivial_scale(float *ts, const float *ts_in, float *amax_out) {
+  *ts = ts_in ? *ts_in : 1.0f;
+  if (amax_out) *amax_out = 0.0f;
+}
+
+hipError_t launch_trivial_scale(float *ts, const float *ts_in, float *amax_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_trivial_scale, dim3(1), dim3(1), 0, s, ts, ts_in, amax_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_eden_scales(const QuantParams &p, uint32_t grid, hipStream_t s) {
   hipLaunchKernelGGL(k_eden_scales, dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
