@@ -49,8 +49,11 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra configurations after the step (profiling runs: then every "
                          "k_gemm launch is one of the step's GEMMs)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="approximate budget for the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="approximate budget for the CPU oracle sample (all threads and one thread)")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="no step, no CPU baseline: only the extra configurations, each timed once as a "
+                         "graph (profiling runs of the kernels outside the step)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="before the warm-up, run one plain fp32 negation of GIB GiB (reads and writes "
                          "exactly that many bytes): the reference that scales the HBM byte counters")
@@ -175,6 +178,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     nv.lib()
+    if args.extras_only:
+        print(json.dumps({"extras_only": other_configs(nv, torch)}), flush=True)
+        return
 
     T, D, O = synth.MLP_SHAPES["X"][0], synth.MLP_SHAPES["X"][1], synth.MLP_SHAPES["W"][0]
     t0 = time.time()
@@ -355,167 +361,236 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
-    """Options beyond the step, timed on the same inputs and buffers (not part
-    of `value`): dY quantized along both axes from one read; IF4 quantization
-    of X and W and the Y GEMM on IF4 operands; Four Over Six and searched
-    block scales for X and W."""
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        total = 0.0
-        for _ in range(reps):
-            a.record(stream)
-            fn()
-            b.record(stream)
-            b.synchronize()
-            total += a.elapsed_time(b)
-        return total / reps
+MALL_BYTES = 256e6      # MI355X memory-side (Infinity) cache
+ROTATE_BYTES = 600e6    # distinct bytes one rotation of copies touches
 
+
+def graph_time(torch, fns, min_calls=20, replays=5):
+    """GPU time per call, in ms, of the calls fns[0], fns[1], ... repeated
+    round-robin: at least `min_calls` calls captured in one HIP graph (short
+    calls launched one by one from Python would leave the GPU waiting on the
+    host), replayed `replays` times after one untimed replay.  With several
+    fns working on distinct copies of their data, each call finds its input
+    evicted from the memory-side cache by the calls before it."""
+    n = max(min_calls, len(fns))
+    n = (n + len(fns) - 1) // len(fns) * len(fns)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fns[i % len(fns)]()
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * n)
+
+
+def n_copies(bytes_per_copy):
+    """Copies of a call's data so that one round over them touches more
+    than the memory-side cache holds (1 if one copy already does)."""
+    if bytes_per_copy >= 2 * MALL_BYTES:
+        return 1
+    return max(1, int(np.ceil(ROTATE_BYTES / bytes_per_copy)))
+
+
+def _q_entry(x, ms, what, copies, bytes_per_elem=BYTES_PER_ELEM_BF16):
+    gbs = x.numel() * bytes_per_elem / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+            "shape_in": list(x.shape), "copies": copies, "what": what}
+
+
+def _g_entry(flops, ms, what, copies):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 3),
+            "copies": copies, "what": what}
+
+
+def _qbuf(nv, torch, x, axis, rounding, dev):
+    R, K = (x.shape[0], x.shape[1]) if axis == 0 else (x.shape[1], x.shape[0])
+    q = nv.QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
+                   torch.empty(1, dtype=torch.float32, device=dev))
+    w = torch.empty(nv.workspace_size(x.shape[0], x.shape[1], rounding, axis), dtype=torch.uint8, device=dev)
+    return q, w
+
+
+def rotating_quant(nv, torch, x, call, axis=0, rounding="rtn"):
+    """GPU ms per call of call(x_i, q_i, ws_i) over enough copies (input,
+    output, workspace) of x to defeat the memory-side cache; returns
+    (ms, copies)."""
+    dev = x.device
+    per = x.numel() * (x.element_size() + 0.5625) + (x.numel() // 4 if rounding == "mseden" else 0)
+    k = n_copies(per)
+    xs = [x] + [x.clone() for _ in range(k - 1)]
+    bufs = [_qbuf(nv, torch, x, axis, rounding, dev) for _ in range(k)]
+    fns = [(lambda xi=xi, b=b: call(xi, b[0], b[1])) for xi, b in zip(xs, bufs)]
+    ms = graph_time(torch, fns)
+    del xs, bufs, fns
+    return ms, k
+
+
+def extras(nv, torch, stream, X, W, dY, signs, outs, wss, reps):
+    """Options beyond the step, timed on the same inputs (not part of
+    `value`): dY quantized along both axes from one read; IF4 quantization of
+    X and W and the Y GEMM on IF4 operands; Four Over Six and searched block
+    scales for X and W; the Y GEMM writing NVFP4.  Calls on W (90 MB, which
+    the 256 MB memory-side cache would hold between calls) rotate over
+    copies of it."""
+    dev = X.device
     res = {}
     # dY along both axes from one read (the step quantizes it twice)
     qr, qc = outs["qdYr"], outs["qdYc"]
-    wsd = torch.empty(nv.workspace_size_dual(dY.shape[0], dY.shape[1]), dtype=torch.uint8, device=dY.device)
-    ms = timed(lambda: nv.quantize_nvfp4_dual(dY, rht_signs=signs, seed=1004, stream_id=0, out_rows=qr,
-                                              out_cols=qc, workspace=wsd))
-    alg = dY.numel() * (2.0 + 2 * 0.5625)
-    res["dY_dual_axis"] = {"ms": round(ms, 4), "GB/s": round(alg / (ms * 1e-3) / 1e9, 1),
-                           "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
-                           "bytes_per_elem": 3.125, "shape_in": list(dY.shape),
-                           "what": "RHT + MS-EDEN of dY along rows and columns from one read "
-                                   "(input once, two sets of codes and scales)"}
+    wsd = torch.empty(nv.workspace_size_dual(dY.shape[0], dY.shape[1]), dtype=torch.uint8, device=dev)
+    ms = graph_time(torch, [lambda: nv.quantize_nvfp4_dual(dY, rht_signs=signs, seed=1004, stream_id=0,
+                                                           out_rows=qr, out_cols=qc, workspace=wsd)], min_calls=3)
+    res["dY_dual_axis"] = _q_entry(dY, ms, "RHT + MS-EDEN of dY along rows and columns from one read (input once, "
+                                   "two sets of codes and scales)", 1, bytes_per_elem=2.0 + 2 * 0.5625)
+    res["dY_dual_axis"]["bytes_per_elem"] = 3.125
     del wsd
     # the Y GEMM with its output coded as NVFP4 in the same kernel (RTN along
     # N, the tensor scale from a first call's max |Y|), on the step's operands
-    Mq, Nq = X.shape[0], W.shape[0]
-    ymax = torch.zeros(1, dtype=torch.float32, device=X.device)
-    qy = nv.QTensor(torch.empty((Mq, Nq // 2), dtype=torch.uint8, device=X.device),
-                    torch.empty((Mq, Nq // 16), dtype=torch.uint8, device=X.device),
-                    torch.ones(1, dtype=torch.float32, device=X.device), nv.FORMAT_NVFP4)
+    Mq, Nq, Kq = X.shape[0], W.shape[0], X.shape[1]
+    ymax = torch.zeros(1, dtype=torch.float32, device=dev)
+    qy = nv.QTensor(torch.empty((Mq, Nq // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((Mq, Nq // 16), dtype=torch.uint8, device=dev),
+                    torch.ones(1, dtype=torch.float32, device=dev), nv.FORMAT_NVFP4)
     nv.gemm_nvfp4_rtn(outs["qX"], outs["qW"], qy.tensor_scale, amax_out=ymax, out=qy)
     qy.tensor_scale.copy_(ymax / 2688.0)
-    ms = timed(lambda: nv.gemm_nvfp4_rtn(outs["qX"], outs["qW"], qy.tensor_scale, amax_out=ymax, out=qy))
-    fl = 2.0 * Mq * Nq * X.shape[1]
-    res["gemm_Y_nvfp4_out"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
-                               "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
-                               "what": "Y = X W^T written as NVFP4 (RTN along N with a given tensor scale, "
-                                       "max |Y| out) by the GEMM itself instead of bf16"}
+    ms = graph_time(torch, [lambda: nv.gemm_nvfp4_rtn(outs["qX"], outs["qW"], qy.tensor_scale, amax_out=ymax,
+                                                      out=qy)], min_calls=2)
+    res["gemm_Y_nvfp4_out"] = _g_entry(2.0 * Mq * Nq * Kq, ms, "Y = X W^T written as NVFP4 (RTN along N with a "
+                                       "given tensor scale, max |Y| out) by the GEMM itself instead of bf16", 1)
     del qy
     # IF4 forward operands (the output buffers of the step are reused), then
     # the Y GEMM on them through the INT-flag-aware entry point
     qa = nv.quantize_if4(X, out=outs["qX"], workspace=wss["qX"])
     qb = nv.quantize_if4(W, out=outs["qW"], workspace=wss["qW"])
-    Yb = torch.empty((X.shape[0], W.shape[0]), dtype=torch.bfloat16, device=X.device)
-    ms = timed(lambda: nv.gemm_nvfp4(qa, qb, out=Yb))
-    fl = 2.0 * X.shape[0] * W.shape[0] * X.shape[1]
-    res["gemm_Y_if4"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
-                         "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
-                         "what": "Y = X W^T, both operands IF4 (INT-flagged blocks decoded by table)"}
-    for name, x, q in (("X_if4", X, "qX"), ("W_if4", W, "qW")):
-        ms = timed(lambda: nv.quantize_if4(x, out=outs[q], workspace=wss[q]))
-        gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
-        res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                     "shape_in": list(x.shape), "what": "IF4 (FP4/INT4 per 16-group), axis 0"}
+    Yb = torch.empty((Mq, Nq), dtype=torch.bfloat16, device=dev)
+    ms = graph_time(torch, [lambda: nv.gemm_nvfp4(qa, qb, out=Yb)], min_calls=2)
+    res["gemm_Y_if4"] = _g_entry(2.0 * Mq * Nq * Kq, ms, "Y = X W^T, both operands IF4 (INT-flagged blocks "
+                                 "decoded by table)", 1)
     del Yb
+    for name, x in (("X_if4", X), ("W_if4", W)):
+        ms, k = rotating_quant(nv, torch, x, lambda xi, q, w: nv.quantize_if4(xi, out=q, workspace=w))
+        res[name] = _q_entry(x, ms, "IF4 (FP4/INT4 per 16-group), axis 0", k)
     for rule, what in (("4over6", "RTN, Four Over Six block scaling, axis 0"),
                        ("search", "RTN, block scale searched over 19 E4M3 bytes, axis 0")):
-        for name, x, q in (("X_" + rule, X, "qX"), ("W_" + rule, W, "qW")):
-            ms = timed(lambda: nv.quantize_nvfp4(x, scale_rule=rule, out=outs[q], workspace=wss[q]))
-            gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
-            res[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                         "shape_in": list(x.shape), "what": what}
+        for name, x in (("X_" + rule, X), ("W_" + rule, W)):
+            ms, k = rotating_quant(nv, torch, x, lambda xi, q, w, r=rule: nv.quantize_nvfp4(
+                xi, scale_rule=r, out=q, workspace=w))
+            res[name] = _q_entry(x, ms, what, k)
     res.update(other_configs(nv, torch))
+    return res
+
+
+def small_config(nv, torch):
+    """The 256 x 256 fp32 correctness case (N(0,1), seed 0), RTN and SR
+    (seed 0, stream 0), no rotation: a latency case.  Per call: GPU time
+    back to back in a HIP graph, and the median of 200 single calls timed
+    with events around each (what one call costs on an idle stream)."""
+    from nvfp4_bit_block_amd import synth
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(synth.gaussian(256, 256, seed=0)).to(dev)
+    res = {}
+    for rnd in ("rtn", "sr"):
+        q, w = _qbuf(nv, torch, x, 0, rnd, dev)
+        call = (lambda r=rnd, q=q, w=w: nv.quantize_nvfp4(x, rounding=r, seed=0, stream_id=0, out=q, workspace=w))
+        ms_graph = graph_time(torch, [call], min_calls=100)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        single = []
+        for _ in range(200):
+            a.record()
+            call()
+            b.record()
+            b.synchronize()
+            single.append(a.elapsed_time(b))
+        res["small_256_" + rnd] = {"us_per_call_graph": round(ms_graph * 1e3, 2),
+                                   "us_single_call_median": round(float(np.median(single)) * 1e3, 2),
+                                   "shape_in": [256, 256], "dtype_in": "fp32",
+                                   "what": f"256x256 fp32 N(0,1), {rnd.upper()}, no rotation: maximum pass "
+                                           "+ coding pass"}
     return res
 
 
 def other_configs(nv, torch):
     """The other workloads of the method's configurations, each on its own
-    seeded inputs (synth.py): the 4096x4096 gradient (rows, rotation, SR and
-    MS-EDEN), the 8192x8192 weight (IF4, RTN) and the weight gradient of a
-    Llama-like linear (dY, X 16384x4096 column-wise with rotation and
-    MS-EDEN, then dW = dY^T X, fp32)."""
+    seeded inputs (synth.py), rotating over copies so that no call finds
+    its data in the memory-side cache: the 256x256 correctness case
+    (latency), the 4096x4096 gradient (rows, rotation: SR, MS-EDEN, and IF4
+    with SR and with MS-EDEN), the 8192x8192 weight (IF4, RTN) and the weight
+    gradient of a Llama-like linear (dY, X 16384x4096 column-wise with
+    rotation and MS-EDEN, then dW = dY^T X, fp32)."""
     from nvfp4_bit_block_amd import synth
     dev = torch.device("cuda:0")
-    res = {}
-
-    def timed(fn, per_graph=20, replays=10):
-        """GPU time per call: these calls are short enough that launching
-        them one by one from Python would leave the GPU waiting for the host,
-        so they are captured in a HIP graph of `per_graph` calls and the
-        graph is replayed (the calls launch kernels only)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(per_graph):
-                fn()
-        graph.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(replays):
-            graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / (replays * per_graph)
-
-    def q_entry(x, ms, what):
-        gbs = x.numel() * BYTES_PER_ELEM_BF16 / (ms * 1e-3) / 1e9
-        return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                "shape_in": list(x.shape), "what": what}
-
-    def buffers(x, rnd, axis):
-        R, K = (x.shape[0], x.shape[1]) if axis == 0 else (x.shape[1], x.shape[0])
-        q = nv.QTensor(torch.empty((R, K // 2), dtype=torch.uint8, device=dev),
-                       torch.empty((R, K // 16), dtype=torch.uint8, device=dev),
-                       torch.empty(1, dtype=torch.float32, device=dev))
-        w = torch.empty(nv.workspace_size(x.shape[0], x.shape[1], rnd, axis), dtype=torch.uint8, device=dev)
-        return q, w
-
+    res = small_config(nv, torch)
     g, gs = synth.gradient(4096, 4096, seed=1)
     G = torch.from_numpy(g).to(dev).to(torch.bfloat16)
     for rnd in ("sr", "mseden"):
-        q, w = buffers(G, rnd, 0)
-        ms = timed(lambda: nv.quantize_nvfp4(G, rounding=rnd, rht_signs=gs, seed=1, out=q, workspace=w))
-        res["gradient_4096_" + rnd] = q_entry(G, ms, f"4096x4096 gradient (5 % outliers x10), RHT + {rnd}, rows")
+        ms, k = rotating_quant(nv, torch, G, lambda xi, q, w, r=rnd: nv.quantize_nvfp4(
+            xi, rounding=r, rht_signs=gs, seed=1, out=q, workspace=w), rounding=rnd)
+        res["gradient_4096_" + rnd] = _q_entry(G, ms, f"4096x4096 gradient (5 % outliers x10), RHT + {rnd}, rows",
+                                               k)
+        ms, k = rotating_quant(nv, torch, G, lambda xi, q, w, r=rnd: nv.quantize_if4(
+            xi, rounding=r, rht_signs=gs, seed=1, out=q, workspace=w), rounding=rnd)
+        res["gradient_4096_if4_" + rnd] = _q_entry(G, ms, f"4096x4096 gradient, RHT + IF4 with {rnd}, rows", k)
     del G
     Wt = torch.from_numpy(synth.weight(8192, 8192, seed=2)).to(dev).to(torch.bfloat16)
-    q, w = buffers(Wt, "rtn", 0)
-    ms = timed(lambda: nv.quantize_if4(Wt, out=q, workspace=w))
-    res["weight_8192_if4"] = q_entry(Wt, ms, "8192x8192 Student-t weight, IF4 RTN, rows")
-    del Wt, q, w
+    ms, k = rotating_quant(nv, torch, Wt, lambda xi, q, w: nv.quantize_if4(xi, out=q, workspace=w))
+    res["weight_8192_if4"] = _q_entry(Wt, ms, "8192x8192 Student-t weight, IF4 RTN, rows", k)
+    del Wt
     dy, x, ws = synth.wgrad(16384, 4096, seed=3)
     dYw = torch.from_numpy(dy).to(dev).to(torch.bfloat16)
     Xw = torch.from_numpy(x).to(dev).to(torch.bfloat16)
-    qw = {}
     for name, t in (("wgrad_dY_cols", dYw), ("wgrad_X_cols", Xw)):
-        q, w = qw[name] = buffers(t, "mseden", 1)
-        ms = timed(lambda: nv.quantize_nvfp4(t, rounding="mseden", axis=1, rht_signs=ws, seed=3, out=q,
-                                             workspace=w))
-        res[name] = q_entry(t, ms, "16384x4096, RHT + MS-EDEN along the 16384 rows (weight gradient operand)")
-    qd, qx = qw["wgrad_dY_cols"][0], qw["wgrad_X_cols"][0]
-    dW = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
-    ms = timed(lambda: nv.gemm_nvfp4(qd, qx, out=dW))
-    fl = 2.0 * 4096 * 4096 * 16384
-    res["wgrad_gemm_dW"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
-                            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 3),
-                            "what": "dW = dY^T X [4096 x 4096], K = 16384, fp32 out: 256 tiles, one per CU"}
+        ms, k = rotating_quant(nv, torch, t, lambda xi, q, w: nv.quantize_nvfp4(
+            xi, rounding="mseden", axis=1, rht_signs=ws, seed=3, out=q, workspace=w), axis=1, rounding="mseden")
+        res[name] = _q_entry(t, ms, "16384x4096, RHT + MS-EDEN along the 16384 rows (weight gradient operand)", k)
+    qd = nv.quantize_nvfp4(dYw, rounding="mseden", axis=1, rht_signs=ws, seed=3)
+    qx = nv.quantize_nvfp4(Xw, rounding="mseden", axis=1, rht_signs=ws, seed=3)
+    ops = qd.codes.numel() + qd.scales.numel() + qx.codes.numel() + qx.scales.numel()
+    k = n_copies(ops + 4096 * 4096 * 4)
+    pairs = [(qd, qx)] + [(nv.QTensor(qd.codes.clone(), qd.scales.clone(), qd.tensor_scale.clone()),
+                           nv.QTensor(qx.codes.clone(), qx.scales.clone(), qx.tensor_scale.clone()))
+                          for _ in range(k - 1)]
+    outs = [torch.empty((4096, 4096), dtype=torch.float32, device=dev) for _ in range(k)]
+    ms = graph_time(torch, [(lambda a=a, b=b, o=o: nv.gemm_nvfp4(a, b, out=o)) for (a, b), o in zip(pairs, outs)])
+    res["wgrad_gemm_dW"] = _g_entry(2.0 * 4096 * 4096 * 16384, ms, "dW = dY^T X [4096 x 4096], K = 16384, fp32 "
+                                    "out: 256 tiles, one per CU", k)
     return res
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(Xh, Wh, dYh, signs, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the same step:
     the same six quantizations restricted to slices of the inputs (each
-    slice quantized as its own tensor), and sampled dW outputs computed one
-    by one.  A small calibration pass sizes the slices so that the measured
-    pass takes about `budget_s` seconds."""
+    slice quantized as its own tensor), on all of the host's threads and on
+    one thread, each the median of 3 runs; and sampled dW outputs computed
+    one by one.  A calibration pass sizes the slices so that the measured
+    runs take about `budget_s` seconds in all."""
     import oracle
     from nvfp4_bit_block_amd import synth
     w = oracle.signs_words(signs)
@@ -546,12 +621,23 @@ def cpu_baseline(Xh, Wh, dYh, signs, budget_s):
             b_q += xb.size * BYTES_PER_ELEM_BF16
         return t_q, b_q
 
+    def measured(threads, share):
+        """Median of 3 runs on a slice sized to `share` of the budget."""
+        oracle.set_num_threads(threads)
+        t_cal, _ = run(128)
+        rows = int(128 * max(1.0, share * budget_s / 3 / max(t_cal, 1e-3)))
+        rows = max(128, min(T, rows // 128 * 128))
+        runs = [run(rows) for _ in range(3)]
+        t_med = sorted(r[0] for r in runs)[1]
+        b = runs[0][1]
+        return {"GB/s": b / t_med / 1e9, "rows": rows, "elements": b / BYTES_PER_ELEM_BF16,
+                "labels": "; ".join(j[0] for j in jobs(rows)), "seconds": [round(r[0], 3) for r in runs]}
+
     t_start = time.perf_counter()
-    t_cal, _ = run(128)
-    rows = int(128 * max(1.0, 0.8 * budget_s / max(t_cal, 1e-3)))
-    rows = max(128, min(T, rows // 128 * 128))
-    t_q, b_q = run(rows)
-    labels = "; ".join(j[0] for j in jobs(rows))
+    all_threads = oracle.num_threads()
+    full = measured(all_threads, 0.5)
+    one = measured(1, 0.5)
+    oracle.set_num_threads(all_threads)
     # GEMM: sampled output entries of dW (K = T), one by one
     qa = oracle.quantize(synth.to_bf16_f32(dYh[:, :64]), rounding=oracle.MSEDEN, axis=1, rht_on=True,
                          signs_w=w)
@@ -563,10 +649,15 @@ def cpu_baseline(Xh, Wh, dYh, signs, budget_s):
     t = time.perf_counter()
     oracle.gemm_entries(qa, qb, im, in_)
     t_g = time.perf_counter() - t
-    return {"value": round(b_q / t_q / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"quantize {labels} (bf16 inputs, {b_q / 2.5625 / 1e6:.1f} M elements); "
-                      f"gemm: {n_ent} dW entries one by one (K={T})",
+    return {"value": round(full["GB/s"], 4), "unit": "GB/s", "cores": all_threads, "kind": "oracle",
+            "sample": f"quantize {full['labels']} (bf16 inputs, {full['elements'] / 1e6:.1f} M elements), "
+                      f"median of 3 runs on {all_threads} threads; gemm: {n_ent} dW entries one by one (K={T})",
+            "runs_s": full["seconds"],
+            "value_1thread": round(one["GB/s"], 4),
+            "sample_1thread": f"quantize {one['labels']} ({one['elements'] / 1e6:.1f} M elements), median of "
+                              f"3 runs on 1 thread",
+            "runs_1thread_s": one["seconds"],
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(),
             "gemm_TFLOP/s": round(n_ent * 2.0 * T / t_g / 1e12, 6),
             "seconds": round(time.perf_counter() - t_start, 1)}
 

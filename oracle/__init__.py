@@ -79,6 +79,8 @@ def lib():
     L.orc_gemm_full.argtypes = [_P, _P, _F32, _P, _P, _F32, _I64, _I64, _I64, _INT, _P]
     L.orc_num_threads.restype = _INT
     L.orc_num_threads.argtypes = []
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads.argtypes = [_INT]
     _lib = L
     return L
 
@@ -279,3 +281,7 @@ def gemm_full(a, b, fmt=FMT_NVFP4):
 
 def num_threads():
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n):
+    lib().orc_set_num_threads(int(n))

@@ -46,6 +46,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads the parallel loops below use from now on (the CPU baseline times
+ * the oracle on one thread and on all of them). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ======================================================================
  * Element and scale formats
  * ==================================================================== */

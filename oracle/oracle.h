@@ -75,6 +75,7 @@ int orc_gemm_full(const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
                   int64_t M, int64_t N, int64_t K, int format, double *out);
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
