@@ -374,6 +374,46 @@ def test_scale_search_keeps_the_window_minimum(orc):
     assert moved > 0
 
 
+@pytest.mark.parametrize("kind", ["gaussian", "heavy"])
+def test_scale_search_reconstruction_scale_cannot_improve(orc, kind):
+    """The palettes page's low-error corner also applies the per-block
+    reconstruction scale that minimizes error (least squares for the kept
+    codes).  With E4M3 block scales and codes re-rounded at every searched
+    scale, that step cannot lower the error: the least-squares scale rounded
+    to either neighbouring E4M3 value, with the kept codes, is never better
+    than the searched minimum.  (Reason: at any E4M3 scale in the window,
+    elementwise-nearest codes are at least as good as any other codes, and
+    the search has tried that scale with them.)  20,000 blocks in float64."""
+    if kind == "gaussian":
+        x = synth.gaussian(1250, 256, seed=71)
+    else:
+        x = synth.weight(1250, 256, seed=72)
+    q = orc.quantize(x, fmt=orc.FMT_NVFP4_SEARCH)
+    ts = np.float64(np.float32(q["ts"]))
+    e4 = np.array([orc.e4m3_value(b) for b in range(127)], dtype=np.float64)
+    grid = np.array([orc.e2m1_value(c) for c in range(16)], dtype=np.float64)
+    z = x.astype(np.float64).reshape(-1, 16)
+    codes = np.empty((x.shape[0], x.shape[1]), np.uint8)
+    codes[:, 0::2] = q["codes"] & 15
+    codes[:, 1::2] = q["codes"] >> 4
+    v = grid[codes.reshape(-1, 16)]                     # signed code values
+    e = q["scales"].reshape(-1).astype(np.int64)
+    S = e4[e] * ts
+    sse = ((z - v * S[:, None]) ** 2).sum(axis=1)
+    vv = (v * v).sum(axis=1)
+    keep = vv > 0
+    s_ls = (z * v).sum(axis=1)[keep] / vv[keep] / ts   # least-squares scale, in units of s_t
+    j = np.clip(np.searchsorted(e4, s_ls, side="right") - 1, 0, 125)
+    best_rec = np.full(s_ls.shape, np.inf)
+    for jj in (j, j + 1):
+        Sr = e4[jj] * ts
+        best_rec = np.minimum(best_rec, ((z[keep] - v[keep] * Sr[:, None]) ** 2).sum(axis=1))
+    assert z.shape[0] == 20000
+    assert np.all(best_rec >= sse[keep] * (1 - 1e-6) - 1e-30)
+    # the least-squares scale does differ from the kept one on most blocks
+    assert np.mean(np.abs(s_ls * ts - S[keep]) > 1e-3 * S[keep]) > 0.5
+
+
 def test_if4_int_flag_only_in_if4(orc):
     x = synth.weight(16, 128, seed=13)
     assert np.all(orc.quantize(x)["scales"] < 0x80)
