@@ -34,6 +34,14 @@ __device__ __forceinline__ int ilog2_floor_clamped(float v, int lo) {
 }
 
 // ---------------------------------------------------------------- division
+// The operand of a fallback IEEE division, made opaque so that the compiler
+// keeps the division inside its (rarely taken, wave-uniform) branch instead
+// of computing it for every value and selecting.
+__device__ __forceinline__ float opaque(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // a / d for the constants d = 6 and 7, correctly rounded: q0 = a * fp32(1/d),
 // r = fma(-q0, d, a) (exact), q = fma(r, fp32(1/d), q0).  An exhaustive check
 // over every finite fp32 a >= 2^-119 shows q equals the IEEE quotient for both
@@ -46,7 +54,7 @@ __device__ __forceinline__ float div_by(float a) {
   const float r = __builtin_fmaf(-q0, d, a);
   float q = __builtin_fmaf(r, inv, q0);
   // (IEEE division below the range, when some lane of the wave needs it)
-  if (__builtin_amdgcn_ballot_w64(!(a >= 0x1p-119f)) != 0) q = (a >= 0x1p-119f) ? q : a / d;
+  if (__builtin_amdgcn_ballot_w64(!(a >= 0x1p-119f)) != 0) q = (a >= 0x1p-119f) ? q : opaque(a) / d;
   return q;
 }
 
@@ -82,7 +90,7 @@ __device__ __forceinline__ float rcp_refined(float b) {
 __device__ __forceinline__ float rcp_rn(float b) {
   float y = rcp_refined(b);
   const bool ok = b >= kDivLo && b <= kDivHi;
-  if (__builtin_amdgcn_ballot_w64(!ok) != 0) y = ok ? y : 1.0f / b;
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) y = ok ? y : 1.0f / opaque(b);
   return y;
 }
 
@@ -93,7 +101,31 @@ __device__ __forceinline__ float div_rn(float a, float b) {
   const float r = __builtin_fmaf(-b, q0, a);
   float q = __builtin_fmaf(r, y, q0);
   const bool ok = b >= kDivLo && b <= kDivHi && (a == 0.0f || (a >= kDivLo && a <= kDivHi));
-  if (__builtin_amdgcn_ballot_w64(!ok) != 0) q = ok ? q : a / b;
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) q = ok ? q : opaque(a) / b;
+  return q;
+}
+
+// a / b for many a and one b: the refined reciprocal of b is computed once;
+// the quotients are those of div_rn(a, b).
+struct Divisor {
+  float b, y;
+  bool ok;
+};
+
+__device__ __forceinline__ Divisor make_divisor(float b) {
+  Divisor d;
+  d.b = b;
+  d.y = rcp_refined(b);
+  d.ok = b >= kDivLo && b <= kDivHi;
+  return d;
+}
+
+__device__ __forceinline__ float div_rn(float a, const Divisor &d) {
+  const float q0 = a * d.y;
+  const float r = __builtin_fmaf(-d.b, q0, a);
+  float q = __builtin_fmaf(r, d.y, q0);
+  const bool ok = d.ok && (a == 0.0f || (a >= kDivLo && a <= kDivHi));
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) q = ok ? q : opaque(a) / d.b;
   return q;
 }
 
@@ -125,15 +157,17 @@ __device__ __forceinline__ uint32_t e4m3_ceil_sat(float v) {
 
 // Stochastic rounding onto the E4M3 grid: up iff u16 < frac * 65536, where
 // frac is the (exact) position inside the bracketing gap.
+// (Written without early returns, so that the compiler selects instead of
+// branching per value; for a >= 448 or a <= 0 the rounding's intermediates
+// are discarded.)
 __device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
-  if (!(a > 0.0f)) return 0u;
-  if (a >= 448.0f) return 0x7Eu;
-  int E = ilog2_floor_clamped(a, -6);
-  float y = a * pow2i(3 - E);
-  float f = floorf(y);
-  float p = y - f;
-  int up = ((float)u16 < p * 65536.0f) ? 1 : 0;
-  return (uint32_t)((E + 6) * 8 + (int)f + up);
+  const int E = ilog2_floor_clamped(a, -6);
+  const float y = a * pow2i(3 - E);
+  const float f = floorf(y);
+  const float p = y - f;
+  const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
+  const uint32_t e = (uint32_t)((E + 6) * 8 + (int)f) + up;
+  return (a >= 448.0f) ? 0x7Eu : ((a > 0.0f) ? e : 0u);
 }
 
 // ---------------------------------------------------------------- E2M1
@@ -143,13 +177,13 @@ __device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
 // u16 < frac * 65536 with frac the exact position inside the gap.
 
 __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t u16) {
-  if (a >= 6.0f) return 7u;
-  int E = ilog2_floor_clamped(a, 0);
-  float y = a * pow2i(1 - E);
-  float f = floorf(y);
-  float p = y - f;
-  int up = ((float)u16 < p * 65536.0f) ? 1 : 0;
-  return (uint32_t)(2 * E + (int)f + up);
+  const int E = ilog2_floor_clamped(a, 0);
+  const float y = a * pow2i(1 - E);
+  const float f = floorf(y);
+  const float p = y - f;
+  const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
+  const uint32_t m = (uint32_t)(2 * E + (int)f) + up;
+  return (a >= 6.0f) ? 7u : m;
 }
 
 // Stochastic rounding onto the integers 0..7 (IF4's INT branch): up iff

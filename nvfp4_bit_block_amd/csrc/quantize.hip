@@ -269,11 +269,21 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       const bool use_int = (Si * Si) * tree16(di) < (Sf * Sf) * tree16(df);
       const Philox4 u0 = uniforms8(p.key, (uint64_t)gb * 2u, 0u);
       const Philox4 u1 = uniforms8(p.key, (uint64_t)gb * 2u + 1u, 0u);
+      const bool coded = use_int ? (ei != 0u) : (ef != 0u);
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        // one stochastic rounding, on the kept branch's grid: the integers
+        // are the E2M1 rounding's binade 1 (neighbours f, f + 1) everywhere
         const uint32_t u = uniform_at(i < 8 ? u0 : u1, i & 7);
-        const uint32_t mag = use_int ? (ei ? int4_sr(yi[i], u) : 0u) : (ef ? e2m1_sr(yf[i], u) : 0u);
+        const float y = use_int ? yi[i] : yf[i];
+        const float top = use_int ? 7.0f : 6.0f;
+        const int E = use_int ? 1 : ilog2_floor_clamped(y, 0);
+        const float ys = y * pow2i(1 - E);
+        const float f = floorf(ys);
+        const uint32_t up = ((float)u < (ys - f) * 65536.0f) ? 1u : 0u;
+        const uint32_t mag0 = (uint32_t)f + up + (use_int ? 0u : (uint32_t)(2 * E));
+        const uint32_t mag = coded ? (y >= top ? 7u : mag0) : 0u;
         const uint32_t nib = sign_nib(z[i]) | mag;
         if (i < 8) lo |= nib << (4 * i);
         else hi |= nib << (4 * (i - 8));
@@ -741,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
 
 // ---------------------------------------------------------------- MS-EDEN scales
 // Scale byte of a target t (sign bit: IF4's INT flag, bit 7 of the byte).
-__device__ __forceinline__ uint32_t eden_scale_byte(float t, float s_t, uint32_t u16) {
+__device__ __forceinline__ uint32_t eden_scale_byte(float t, const Divisor &s_t, uint32_t u16) {
   const uint32_t flag = (__float_as_uint(t) >> 24) & 0x80u;
   return e4m3_sr_sat(fminf(div_rn(fabsf(t), s_t), 448.0f), u16) | flag;
 }
@@ -762,6 +772,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     const float m = block_max(partials_max(p.rpartial, p.npartial), red, kThreads);
     if (threadIdx.x == 0) *p.amax_out = m;
   }
+  const Divisor dst = make_divisor(s_t);
   // Whole calls (8 blocks each): the next call's targets are loaded while
   // this one is coded (clamped to the last call, so the load is unconditional).
   const uint32_t nfull = p.nblocks / 8u;
@@ -772,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t e = eden_scale_byte(t[j], s_t, uniform_at(u, j));
+      const uint32_t e = eden_scale_byte(t[j], dst, uniform_at(u, j));
       if (j < 4) lo |= e << (8 * j);
       else hi |= e << (8 * (j - 4));
     }
@@ -794,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
   if (p.nblocks % 8u && blockIdx.x * kThreads + threadIdx.x == nfull % stride) {
     const Philox4 u = uniforms8(p.key, (uint64_t)nfull, 1u);
     for (uint32_t j = 0; nfull * 8u + j < p.nblocks; ++j)
-      p.scales[nfull * 8u + j] = (uint8_t)eden_scale_byte(p.tb[nfull * 8u + j], s_t, uniform_at(u, (int)j));
+      p.scales[nfull * 8u + j] = (uint8_t)eden_scale_byte(p.tb[nfull * 8u + j], dst, uniform_at(u, (int)j));
   }
 }
 
