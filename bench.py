@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="before the warm-up, run one plain fp32 negation of GIB GiB (reads and writes "
                          "exactly that many bytes): the reference that scales the HBM byte counters")
+    ap.add_argument("--activity-from", metavar="PMC_DIR",
+                    help="no benchmark: print a markdown table of the activity counters of one rocprofv3 "
+                         "--pmc run of this script (GRBM_GUI_ACTIVE, SQ_* counters), per library kernel")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: read two rocprofv3 --pmc outputs of this script (FETCH_SIZE, "
                          "then WRITE_SIZE, both run with the --copy-calibration given here) and write "
@@ -161,10 +164,88 @@ def write_traffic(fetch_dir, write_dir, cal_gib):
     print(f"wrote {path}")
 
 
+def compiler_registers():
+    """kernel symbol -> (VGPRs, AGPRs, SGPRs, LDS bytes) from the device
+    assembly the build keeps (the compiler's resource metadata)."""
+    import glob
+    import re
+    out = {}
+    for f in glob.glob(os.path.join(ROOT, "nvfp4_bit_block_amd", "_build", "*.s")):
+        name = None
+        vals = {}
+        for line in open(f):
+            m = re.match(r"\s+\.(name|vgpr_count|agpr_count|sgpr_count|group_segment_fixed_size):\s+(\S+)", line)
+            if not m:
+                continue
+            k, v = m.group(1), m.group(2)
+            if k == "group_segment_fixed_size":
+                if name and vals:
+                    out[name] = vals
+                vals, name = {"lds": int(v)}, None
+            elif k == "name":
+                name = v
+            else:
+                vals[k] = int(v)
+            if name and "vgpr_count" in vals and "sgpr_count" in vals:
+                out[name] = dict(vals)
+    import subprocess
+    names = list(out)
+    try:
+        dem = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
+    except OSError:
+        dem = names
+    return {d.strip(): out[n] for n, d in zip(names, dem)}
+
+
+def write_activity(pmc_dir):
+    """Per-dispatch activity of the library's kernels from one rocprofv3
+    --pmc run, as markdown: duration, clock (GRBM_GUI_ACTIVE counts core
+    clock cycles summed over the 8 XCDs; its window also covers a few
+    microseconds of dispatch and drain around the kernel, so the clock is
+    given only for kernels longer than 200 us), matrix-pipe busy fraction,
+    vector instructions and waits per wave-cycle, and the compiler's
+    register counts."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    acc = {}
+    for r in csv.DictReader(open(files[0])):
+        if "nv4::" not in r["Kernel_Name"]:
+            continue
+        key = int(r["Dispatch_Id"])
+        e = acc.setdefault(key, {"name": r["Kernel_Name"], "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                 "c": {}})
+        e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    regs = compiler_registers()
+    print("| Kernel | Duration (us) | Clock (GHz) | MFMA busy | VALU instr. / wave-cycle | s_waitcnt / wave-cycle "
+          "| LDS wait / wave-cycle | VGPR / AGPR / LDS bytes (compiler) |")
+    print("|---|---|---|---|---|---|---|---|")
+    for key in sorted(acc):
+        e = acc[key]
+        c = e["c"]
+        short = e["name"].split("nv4::")[1].split("(")[0]
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        dur = e["dur"]
+        clock = f"{cyc / (dur * 1e-9) / 1e9:.2f}" if dur > 200e3 and cyc else "n/a"
+        busy = f"{c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / (1024 * cyc):.3f}" if cyc else "n/a"
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        valu = f"{c.get('SQ_ACTIVE_INST_VALU', 0.0) / wc:.3f}" if wc else "n/a"
+        wait = f"{c.get('SQ_WAIT_INST_ANY', 0.0) / wc:.3f}" if wc else "n/a"
+        lds = f"{c.get('SQ_WAIT_INST_LDS', 0.0) / wc:.3f}" if wc else "n/a"
+        rg = regs.get(e["name"].strip())
+        r = f"{rg.get('vgpr_count', '?')} / {rg.get('agpr_count', 0)} / {rg.get('lds', '?')}" if rg else "?"
+        print(f"| `{short}` | {dur / 1e3:.1f} | {clock} | {busy} | {valu} | {wait} | {lds} | {r} |")
+
+
 def main():
     args = parse()
     if args.traffic_from:
         write_traffic(*args.traffic_from, args.copy_calibration)
+        return
+    if args.activity_from:
+        write_activity(args.activity_from)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the quantizers and the "
@@ -280,6 +361,7 @@ def main():
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    progress(f"{args.warmup} warm-up steps done")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     all_marks = []
@@ -290,6 +372,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
+    progress(f"{args.steps} timed steps: {ms_per_step:.3f} ms per step")
 
     qms = {n: 0.0 for n, *_ in plan}
     gms = {n: 0.0 for n, *_ in gemms}
@@ -361,6 +444,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def progress(msg):
+    """A progress line on stderr (long profiling runs stay visibly alive)."""
+    print(f"# {msg}", file=sys.stderr, flush=True)
+
+
 MALL_BYTES = 256e6      # MI355X memory-side (Infinity) cache
 ROTATE_BYTES = 600e6    # distinct bytes one rotation of copies touches
 
@@ -406,12 +494,14 @@ def n_copies(bytes_per_copy):
 
 
 def _q_entry(x, ms, what, copies, bytes_per_elem=BYTES_PER_ELEM_BF16):
+    progress(f"{what}: {ms:.4f} ms")
     gbs = x.numel() * bytes_per_elem / (ms * 1e-3) / 1e9
     return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
             "shape_in": list(x.shape), "copies": copies, "what": what}
 
 
 def _g_entry(flops, ms, what, copies):
+    progress(f"{what}: {ms:.4f} ms")
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 3),
             "copies": copies, "what": what}

@@ -69,10 +69,13 @@ def _device_asm(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES) + 1)) as ex:
-        asm = ex.submit(_device_asm, "quantize.hip", verbose)
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES) + 3)) as ex:
+        # device assembly of the kernel sources (build checks; register counts
+        # for the profile summaries)
+        asm = [ex.submit(_device_asm, f, verbose) for f in ("quantize.hip", "gemm.hip", "dequantize.hip")]
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-        asm.result()
+        for a in asm:
+            a.result()
     tdir = _torch_lib_dir()
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     link = ["g++", "-shared", "-o", LIB + ".tmp"] + objs
