@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--activity-from", metavar="PMC_DIR",
                     help="no benchmark: print a markdown table of the activity counters of one rocprofv3 "
                          "--pmc run of this script (GRBM_GUI_ACTIVE, SQ_* counters), per library kernel")
+    ap.add_argument("--per-kernel", action="store_true",
+                    help="with --activity-from: one row per kernel instance (means over its launches)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: read two rocprofv3 --pmc outputs of this script (FETCH_SIZE, "
                          "then WRITE_SIZE, both run with the --copy-calibration given here) and write "
@@ -197,7 +199,7 @@ def compiler_registers():
     return {d.strip(): out[n] for n, d in zip(names, dem)}
 
 
-def write_activity(pmc_dir):
+def write_activity(pmc_dir, per_kernel=False):
     """Per-dispatch activity of the library's kernels from one rocprofv3
     --pmc run, as markdown: duration, clock (GRBM_GUI_ACTIVE counts core
     clock cycles summed over the 8 XCDs; its window also covers a few
@@ -219,16 +221,29 @@ def write_activity(pmc_dir):
                                  "c": {}})
         e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     regs = compiler_registers()
-    print("| Kernel | Duration (us) | Clock (GHz) | MFMA busy | VALU instr. / wave-cycle | s_waitcnt / wave-cycle "
+    if per_kernel:
+        # one row per instance: sums of the counters and durations over its launches
+        merged = {}
+        for key in sorted(acc):
+            e = acc[key]
+            m = merged.setdefault(e["name"], {"name": e["name"], "dur": 0, "c": {}, "n": 0, "long": 0})
+            m["n"] += 1
+            m["dur"] += e["dur"]
+            for k, v in e["c"].items():
+                m["c"][k] = m["c"].get(k, 0.0) + v
+        acc = {i: m for i, m in enumerate(sorted(merged.values(), key=lambda m: -m["dur"]))}
+    print("| Kernel | " + ("Launches | Mean duration (us)" if per_kernel else "Duration (us)") +
+          " | Clock (GHz) | MFMA busy | VALU instr. / wave-cycle | s_waitcnt / wave-cycle "
           "| LDS wait / wave-cycle | VGPR / AGPR / LDS bytes (compiler) |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|---|" + ("---|" if per_kernel else ""))
     for key in sorted(acc):
         e = acc[key]
         c = e["c"]
         short = e["name"].split("nv4::")[1].split("(")[0]
         cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
         dur = e["dur"]
-        clock = f"{cyc / (dur * 1e-9) / 1e9:.2f}" if dur > 200e3 and cyc else "n/a"
+        n = e.get("n", 1)
+        clock = f"{cyc / (dur * 1e-9) / 1e9:.2f}" if dur / n > 200e3 and cyc else "n/a"
         busy = f"{c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / (1024 * cyc):.3f}" if cyc else "n/a"
         wc = c.get("SQ_WAVE_CYCLES", 0.0)
         valu = f"{c.get('SQ_ACTIVE_INST_VALU', 0.0) / wc:.3f}" if wc else "n/a"
@@ -236,7 +251,8 @@ def write_activity(pmc_dir):
         lds = f"{c.get('SQ_WAIT_INST_LDS', 0.0) / wc:.3f}" if wc else "n/a"
         rg = regs.get(e["name"].strip())
         r = f"{rg.get('vgpr_count', '?')} / {rg.get('agpr_count', 0)} / {rg.get('lds', '?')}" if rg else "?"
-        print(f"| `{short}` | {dur / 1e3:.1f} | {clock} | {busy} | {valu} | {wait} | {lds} | {r} |")
+        head = f"{n} | {dur / n / 1e3:.1f}" if per_kernel else f"{dur / 1e3:.1f}"
+        print(f"| `{short}` | {head} | {clock} | {busy} | {valu} | {wait} | {lds} | {r} |")
 
 
 def main():
@@ -245,7 +261,7 @@ def main():
         write_traffic(*args.traffic_from, args.copy_calibration)
         return
     if args.activity_from:
-        write_activity(args.activity_from)
+        write_activity(args.activity_from, args.per_kernel)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the quantizers and the "
