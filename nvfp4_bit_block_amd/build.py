@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions: the quantizers' matrix-core rotation keeps its
+# accumulators in ordinary VGPRs (read by the vector ALU right after), not
+# in the accumulation registers, which would cost a copy per value.
+EXTRA_FLAGS = {"quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _torch_lib_dir():
@@ -43,7 +47,8 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                                              os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,8 +62,9 @@ def _compile(src, verbose):
 def _device_asm(src, verbose):
     """gfx950 assembly of one source, kept in _build/ for the build checks."""
     out = os.path.join(BUILD, os.path.basename(src) + ".s")
-    cmd = [_hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S",
-                                     os.path.join(CSRC, src), "-o", out]
+    cmd = [_hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC,
+                                                              "--cuda-device-only", "-S", os.path.join(CSRC, src),
+                                                              "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

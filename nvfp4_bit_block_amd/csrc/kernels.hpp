@@ -32,7 +32,8 @@ constexpr bool takes_tensor_scale(int m) {
 }
 constexpr bool writes_partials(int m) { return m == kAmax || m == kEden || m == kIf4Eden; }
 
-constexpr int kThreads = 256;      // threads per workgroup of every quantizer
+constexpr int kThreads = 256;      // threads per workgroup of the quantizers
+constexpr int kMxThreads = 256;    // ... of the matrix-core rotation kernels
 constexpr int kMaxPartials = 2048; // workgroups of a pass that writes partials
 // Axis-1 kernels: each lane loads kColWords 32-bit words of each of its 16
 // rows (bf16: 2 columns per word, fp32: 1), so a wave tile is 128 rows x

@@ -26,27 +26,29 @@ namespace nv4 {
 // (all >= 0): its kMaxPartials / kThreads loads are issued together, so the
 // prologue of every workgroup that needs the tensor scale waits on memory
 // once rather than once per load; loads past n read 0 (range-checked).
+template <int NT = kThreads>
 __device__ __forceinline__ float partials_max(const float *v, uint32_t n) {
-  static_assert(kMaxPartials % kThreads == 0, "partials per thread");
+  static_assert(kMaxPartials % NT == 0, "partials per thread");
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void *)v, (short)0, (int)(4 * n), kRsrcWord3);
-  float m[kMaxPartials / kThreads];
+  float m[kMaxPartials / NT];
 #pragma unroll
-  for (int k = 0; k < kMaxPartials / kThreads; ++k)
-    m[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (threadIdx.x + k * kThreads), 0, 0));
+  for (int k = 0; k < kMaxPartials / NT; ++k)
+    m[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (threadIdx.x + k * NT), 0, 0));
   float a = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kMaxPartials / kThreads; ++k) a = fmaxf(a, m[k]);
+  for (int k = 0; k < kMaxPartials / NT; ++k) a = fmaxf(a, m[k]);
   return a;
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ float tensor_scale(const QuantParams &p, float *red) {
   if (p.ts_in) return *p.ts_in;
   if (p.amax_in) {
     const float a = *p.amax_in;
     return (a > 0.0f) ? a / p.top : 1.0f;
   }
-  const float m = block_max(partials_max(p.partial, p.npartial), red, kThreads);
+  const float m = block_max(partials_max<NT>(p.partial, p.npartial), red, NT);
   return (m > 0.0f) ? m / p.top : 1.0f;
 }
 
@@ -110,8 +112,9 @@ __device__ __forceinline__ float raw_absmax(const uint32_t (&w)[N]) {
 
 // MS-EDEN with amax_out: the workgroup's maximum of |x| (the raw input)
 // goes to the second partial array, which k_eden_scales reduces.
+template <int NT = kThreads>
 __device__ __forceinline__ void raw_partial(const QuantParams &p, float araw, float *red) {
-  const float m = block_max(araw, red, kThreads);
+  const float m = block_max(araw, red, NT);
   if (threadIdx.x == 0) p.rpartial[blockIdx.x] = m;
 }
 
@@ -164,6 +167,89 @@ struct RowSink {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), t, 4 * r, 0, 0);
   }
 };
+
+// ---------------------------------------------------------------- MS-EDEN
+// One block's share of MS-EDEN: RTN codes under the exact scale a/6 (IF4:
+// also integers under a/7, keeping the branch with the smaller pairwise
+// squared error) and the block's sums for the correction
+// c = sum z^2 / sum z*zhat over the group.
+struct EdenBlock {
+  uint32_t lo, hi;  // codes
+  float s_b;        // the kept branch's exact scale
+  float N, D;       // sum z^2, sum z*zhat over the block (pairwise, natural order)
+  bool use_int;
+};
+
+template <int MODE>
+__device__ __forceinline__ EdenBlock eden_codes(const float z[16], float a) {
+  constexpr bool IF4 = MODE == kIf4Eden || MODE == kIf4EdenFused;
+  EdenBlock b;
+  b.s_b = div_by<6>(a);
+  const float r = (a > 0.0f) ? rcp_rn(b.s_b) : 0.0f;
+  float nn[16], dd[16], y[16], g[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = z[i] * r;  // r = 0 when a = 0: signed zeros
+  e2m1x16_rne(y, b.lo, b.hi);
+  e2m1x16_value(b.lo, b.hi, g);  // signed grid values
+  b.use_int = false;
+  if constexpr (IF4) {
+    const float si = div_by<7>(a);
+    const float ri = (a > 0.0f) ? rcp_rn(si) : 0.0f;
+    float sqf[16], sqi[16], gi[16];
+    uint32_t ilo = 0, ihi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float df = z[i] - g[i] * b.s_b;
+      sqf[i] = df * df;
+      const uint32_t sn = sign_nib(z[i]);
+      const uint32_t mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
+      gi[i] = sn ? -(float)mi : (float)mi;
+      const float di = z[i] - gi[i] * si;
+      sqi[i] = di * di;
+      if (i < 8) ilo |= (sn | mi) << (4 * i);
+      else ihi |= (sn | mi) << (4 * (i - 8));
+    }
+    b.use_int = tree16(sqi) < tree16(sqf);
+    if (b.use_int) {
+      b.lo = ilo;
+      b.hi = ihi;
+      b.s_b = si;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) g[i] = gi[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float zh = g[i] * b.s_b;
+    nn[i] = z[i] * z[i];
+    dd[i] = z[i] * zh;
+  }
+  b.N = tree16(nn);
+  b.D = tree16(dd);
+  return b;
+}
+
+// The block's outputs from its group's sums N, D: target t = s_b * c
+// (pass 1: codes and t, whose sign bit carries IF4's INT flag) or, with a
+// known tensor scale, the scale byte by stochastic rounding of t / s_t.
+template <int MODE, typename Sink>
+__device__ __forceinline__ void eden_emit(const EdenBlock &b, float N, float D, uint32_t gb, const Sink &out,
+                                          const QuantParams &p, float s_t, float &lmax) {
+  const float c = (D > 0.0f) ? div_rn(N, D) : 1.0f;
+  const float t = b.s_b * c;
+  if constexpr (MODE == kEden || MODE == kIf4Eden) {
+    out.codes(b.lo, b.hi);
+    // the sign bit carries the INT flag (t >= +0, or NaN where the group's
+    // sums overflow, whose sign is the division's)
+    out.target(b.use_int ? -fabsf(t) : fabsf(t));
+    if (out.active) lmax = fmaxf(lmax, t);
+  } else {
+    const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);
+    const uint32_t e = e4m3_sr_sat(fminf(div_rn(t, s_t), 448.0f), uniform_at(u, (int)(gb & 7u)));
+    out.codes(b.lo, b.hi);
+    out.scale(b.use_int ? (e | 0x80u) : e);
+  }
+}
 
 // ---------------------------------------------------------------- one block
 // z: the lane's 16 (rotated) values; gb: its block index in the output
@@ -355,53 +441,8 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       out.codes(blo, bhi);
       out.scale(best_e);
     } else if constexpr (MODE == kEden || MODE == kEdenFused || MODE == kIf4Eden || MODE == kIf4EdenFused) {
-      // RTN codes under the exact scale a/6 (IF4: also integers under a/7,
-      // keeping the branch with the smaller pairwise squared error);
-      // correction c = sum z^2 / sum z*zhat over the group; target
-      // t = (kept exact scale) * c.
-      constexpr bool IF4 = MODE == kIf4Eden || MODE == kIf4EdenFused;
-      float s_b = div_by<6>(a);
-      const float r = (a > 0.0f) ? rcp_rn(s_b) : 0.0f;
-      float nn[16], dd[16], y[16], g[16];
-      uint32_t lo, hi;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = z[i] * r;  // r = 0 when a = 0: signed zeros
-      e2m1x16_rne(y, lo, hi);
-      e2m1x16_value(lo, hi, g);  // signed grid values
-      bool use_int = false;
-      if constexpr (IF4) {
-        const float si = div_by<7>(a);
-        const float ri = (a > 0.0f) ? rcp_rn(si) : 0.0f;
-        float sqf[16], sqi[16], gi[16];
-        uint32_t ilo = 0, ihi = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float df = z[i] - g[i] * s_b;
-          sqf[i] = df * df;
-          const uint32_t sn = sign_nib(z[i]);
-          const uint32_t mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
-          gi[i] = sn ? -(float)mi : (float)mi;
-          const float di = z[i] - gi[i] * si;
-          sqi[i] = di * di;
-          if (i < 8) ilo |= (sn | mi) << (4 * i);
-          else ihi |= (sn | mi) << (4 * (i - 8));
-        }
-        use_int = tree16(sqi) < tree16(sqf);
-        if (use_int) {
-          lo = ilo;
-          hi = ihi;
-          s_b = si;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) g[i] = gi[i];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float zh = g[i] * s_b;
-        nn[i] = z[i] * z[i];
-        dd[i] = z[i] * zh;
-      }
-      float N = tree16(nn), D = tree16(dd);
+      const EdenBlock b = eden_codes<MODE>(z, a);
+      float N = b.N, D = b.D;
       if (!p.group16) {
         N = N + lane_xor<1>(N);
         D = D + lane_xor<1>(D);
@@ -410,20 +451,7 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
         N = N + lane_xor<4>(N);
         D = D + lane_xor<4>(D);
       }
-      const float c = (D > 0.0f) ? div_rn(N, D) : 1.0f;
-      const float t = s_b * c;
-      if constexpr (MODE == kEden || MODE == kIf4Eden) {
-        out.codes(lo, hi);
-        // the sign bit carries the INT flag (t >= +0, or NaN where the group's
-        // sums overflow, whose sign is the division's)
-        out.target(use_int ? -fabsf(t) : fabsf(t));
-        if (active) lmax = fmaxf(lmax, t);
-      } else {
-        const Philox4 u = uniforms8(p.key, (uint64_t)(gb >> 3), 1u);
-        const uint32_t e = e4m3_sr_sat(fminf(div_rn(t, s_t), 448.0f), uniform_at(u, (int)(gb & 7u)));
-        out.codes(lo, hi);
-        out.scale(use_int ? (e | 0x80u) : e);
-      }
+      eden_emit<MODE>(b, N, D, gb, out, p, s_t, lmax);
     }
   }
 }
@@ -533,6 +561,275 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantParams p) {
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
   }
   if constexpr (RAW) raw_partial(p, araw, red);
+}
+
+// ---------------------------------------------------------------- matrix-core rotation
+// For bf16 input the 128-point rotation z = c H diag(s) x (H the Sylvester
+// Hadamard matrix, H[o][k] = (-1)^popcount(o & k), c = 1/sqrt(128)) is a
+// product with a +-1 matrix, which bf16 holds exactly: it runs on the matrix
+// cores (v_mfma_f32_32x32x16_bf16: exact products, fp32 accumulation), and
+// c is applied in fp32 afterwards.  The butterfly stages cost 8 vector
+// instructions per element, about 40 % of an MS-EDEN pass's vector work,
+// on units that the coding needs; the matrix cores are idle in a quantizer.
+// The result matches the butterflies' to fp32 rounding (both round sums of
+// the same exact products), not bit for bit.
+//
+// MFMA D[i][j] = sum_k A[i][k] B[k][j], 32 x 32 x 16: lane l holds
+// A[l % 32][8h + e] and B[8h + e][l % 32] (h = l / 32, e = 0..7), and
+// D[8 (r / 4) + 4h + r % 4][l % 32] in accumulator r.  For a 128-group:
+//   step t (0..7) takes input positions k = in(t, h, e),
+//   chunk n (0..3) gives outputs o = 64 i2 + 16 n + 4 i[4:3] + i[1:0] of
+//   A row i,
+// so that lane (j, h) ends with output 64h + 16n + r in accumulator r of
+// chunk n: the whole 16-block 4h + n of its group j.  Since bits 4 and 5 of
+// k are bits 0 and 1 of t, A for (n, t) is (-1)^popcount(n & t & 3) times A
+// for (0, t): a workgroup keeps A(0, t) and its negation, t = 0..7, in LDS
+// (16 fragments x 64 lanes x 16 bytes).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kRotNorm = 0x1.6a09e6p-4f;  // fp32(1/sqrt(128)) = 0x3DB504F3
+
+__device__ __forceinline__ uint32_t mx_out0(uint32_t i) {
+  return ((i & 4u) << 4) | ((i >> 3) << 2) | (i & 3u);
+}
+
+// Input position (0..127) of operand slot (h, e) in step t.  AXIS 0: the 8
+// slots of a lane are 8 consecutive elements (one 16-byte load); AXIS 1
+// (operands read from LDS one element at a time): slot bit 2 -> position
+// bit 3 and the lane half -> bit 2, which puts the two lane halves' rows
+// four rows apart, on disjoint LDS banks.
+template <int AXIS>
+__device__ __forceinline__ uint32_t mx_in(uint32_t t, uint32_t h, uint32_t e) {
+  if constexpr (AXIS == 0) return 16u * t + 8u * h + e;
+  else return 16u * t + 8u * (e >> 2) + 4u * h + (e & 3u);
+}
+
+typedef uint4 RotFrags[16][64];
+
+template <int AXIS>
+__device__ __forceinline__ void mx_build_frags(const uint32_t sg[4], RotFrags &fr) {
+  for (uint32_t x = threadIdx.x; x < 16u * 64u; x += blockDim.x) {
+    const uint32_t f = x >> 6, l = x & 63u, t = f >> 1, neg = f & 1u;
+    const uint32_t o = mx_out0(l & 31u), h = l >> 5;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (uint32_t e = 0; e < 8; ++e) {
+      const uint32_t k = mx_in<AXIS>(t, h, e);
+      const uint32_t sgn = ((uint32_t)__builtin_popcount(o & k) + ((sg[k >> 5] >> (k & 31u)) & 1u) + neg) & 1u;
+      w[e >> 1] |= (0x3F80u | (sgn << 15)) << (16u * (e & 1u));  // bf16 +-1
+    }
+    fr[f][l] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// The four chunks' accumulators of one group from the 8 steps' B operands.
+__device__ __forceinline__ void mx_rotate(const RotFrags &fr, const uint4 (&xb)[8], uint32_t lane,
+                                          f32x16_t (&acc)[4]) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x16_t{};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb[t]);
+    const bf16x8_t ap = __builtin_bit_cast(bf16x8_t, fr[2 * t][lane]);
+    const bf16x8_t am = __builtin_bit_cast(bf16x8_t, fr[2 * t + 1][lane]);
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((__builtin_popcount(n & t & 3) & 1) ? am : ap, b, acc[n],
+                                                        0, 0, 0);
+  }
+}
+
+// A lane's four consecutive blocks' outputs, stored together.
+struct QuadOut {
+  uint32_t c[8];
+  uint32_t s;
+  float t[4];
+};
+
+struct SlotSink {
+  QuadOut &q;
+  int n;
+  bool active;
+  __device__ __forceinline__ void codes(uint32_t lo, uint32_t hi) const {
+    q.c[2 * n] = lo;
+    q.c[2 * n + 1] = hi;
+  }
+  __device__ __forceinline__ void scale(uint32_t e) const { q.s |= (e & 0xFFu) << (8 * n); }
+  __device__ __forceinline__ void target(float v) const { q.t[n] = v; }
+};
+
+// Code the lane's four blocks (accumulators acc, first block gb0) into q
+// (mx_store writes them).  MS-EDEN's group of 128 is the two lane halves' 4 + 4 blocks: the
+// sums add in the same pairwise tree as the 8-lane groups of the butterfly
+// kernels, ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7)).
+template <int MODE>
+__device__ __forceinline__ void mx_code4(f32x16_t (&acc)[4], uint32_t gb0, bool active, const QuantParams &p,
+                                         float s_t, float &lmax, QuadOut &q) {
+  constexpr bool EDEN = MODE == kEden || MODE == kEdenFused || MODE == kIf4Eden || MODE == kIf4EdenFused;
+  q.s = 0u;
+  if constexpr (EDEN) {
+    EdenBlock b[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      float z[16], a = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = acc[n][r] * kRotNorm;
+        a = fmaxf(a, fabsf(z[r]));
+      }
+      b[n] = eden_codes<MODE>(z, a);
+    }
+    if (p.group16) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) eden_emit<MODE>(b[n], b[n].N, b[n].D, gb0 + n, SlotSink{q, n, active}, p, s_t, lmax);
+    } else {
+      float N = (b[0].N + b[1].N) + (b[2].N + b[3].N);
+      float D = (b[0].D + b[1].D) + (b[2].D + b[3].D);
+      // the partner half's sums (lanes l and l ^ 32 swap)
+      const auto pn = __builtin_amdgcn_permlane32_swap(__float_as_uint(N), __float_as_uint(N), false, false);
+      const auto pd = __builtin_amdgcn_permlane32_swap(__float_as_uint(D), __float_as_uint(D), false, false);
+      N = __uint_as_float(pn[0]) + __uint_as_float(pn[1]);
+      D = __uint_as_float(pd[0]) + __uint_as_float(pd[1]);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) eden_emit<MODE>(b[n], N, D, gb0 + n, SlotSink{q, n, active}, p, s_t, lmax);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      float z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = acc[n][r] * kRotNorm;
+      quant_block<MODE>(z, gb0 + n, SlotSink{q, n, active}, p, s_t, lmax);
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void mx_store(const QuadOut &q, uint32_t gb0, bool active, const QuantParams &p) {
+  if constexpr (MODE != kAmax && MODE != kRot) {
+    if (active) {
+      uint4 *c = reinterpret_cast<uint4 *>(p.codes + (size_t)gb0 * 8);
+      c[0] = make_uint4(q.c[0], q.c[1], q.c[2], q.c[3]);
+      c[1] = make_uint4(q.c[4], q.c[5], q.c[6], q.c[7]);
+      if constexpr (MODE == kEden || MODE == kIf4Eden)
+        *reinterpret_cast<float4 *>(p.tb + gb0) = make_float4(q.t[0], q.t[1], q.t[2], q.t[3]);
+      else
+        *reinterpret_cast<uint32_t *>(p.scales + gb0) = q.s;
+    }
+  }
+}
+
+// Axis 0, bf16 input, rotation on.  A wave tile is 32 consecutive groups of
+// the row-major group order (4096 elements; contiguous in memory for a dense
+// tensor); lane (j, h) rotates group j of the tile and codes its blocks
+// 4h .. 4h+3, so that the tile's codes, scales and targets are contiguous
+// too.  The tile is staged in the wave's 8 KB of LDS by direct-to-LDS loads:
+// load i brings groups 4i .. 4i+3 (1 KB, coalesced); lane l of it takes
+// 16-byte chunk c = (l % 16) ^ ((4i + l / 16) % 16) of group 4i + l / 16 and
+// lands at slot 64i + l.  The MFMA operand of lane (j, h) in step t (chunk
+// 2t + h of group j) is then one ds_read_b128 whose 16 lanes of a quarter
+// wave hit 16 different 16-byte bank groups.  Groups past the last read
+// zeros (dense: the buffer's range check) or the last group (strided), and
+// store nothing.  A tile's outputs are stored in the next iteration, after
+// its successor's loads were issued, so that the wait for a tile's data
+// never waits for the previous tile's stores.  RAW as for k_quant_rows.
+template <int MODE, int RAW = 0>
+__global__ __launch_bounds__(kMxThreads) void k_quant_rows_mx(QuantParams p) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __shared__ RotFrags fr;
+  __shared__ uint4 stage[kMxThreads / kWave][512];
+  // (the reductions before and after the loop use the stage's first bytes)
+  float *const red = reinterpret_cast<float *>(&stage[0][0]);
+  float s_t = 1.0f;
+  if constexpr (takes_tensor_scale(MODE)) {
+    s_t = tensor_scale<kMxThreads>(p, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  }
+  mx_build_frags<0>(p.sg, fr);
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63u, j = lane & 31u, h = lane >> 5;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t G = p.K16 >> 3;  // groups per row
+  const uint32_t nf = p.R * G;    // groups
+  const uint32_t ntiles = (nf + 31u) >> 5;
+  const uint32_t waves = gridDim.x * (kMxThreads / kWave);
+  const bool dense = p.ld == (int64_t)p.K;
+  // load i, lane l: group 4i + a4 (a4 = l / 16), 16-byte chunk
+  // (l % 16) ^ (4i + a4) (i < 4; i + 4 alike), at byte
+  // 1024 i + 256 a4 + 16 ((l % 16) ^ (4i + a4)) = 1024 i + (vbase ^ 64 i)
+  const uint32_t a4 = lane >> 4;
+  const uint32_t vbase = 256u * a4 + ((16u * (lane & 15u)) ^ (16u * a4));
+  auto load_tile = [&](uint32_t T) {
+    if (dense) {
+      const uint64_t base = (uint64_t)T * 8192u, total = (uint64_t)nf * 256u;
+      const uint64_t left = total - base;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(static_cast<const uint8_t *>(p.x) + base), (short)0, (int)(left < 8192u ? left : 8192u),
+          kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&stage[w][64 * i], 16,
+                                                 (vbase ^ (64u * (i & 3))) + 1024u * (i & 3), 4096u * (i >> 2), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t f = 32u * T + 4u * i + a4;
+        const uint32_t fl = f < nf ? f : nf - 1u;
+        const uint32_t row = fdiv(8u * fl, p.k16div);
+        const uint32_t c = (lane & 15u) ^ ((4u * i + a4) & 15u);
+        const uint16_t *src = static_cast<const uint16_t *>(p.x) + (size_t)row * p.ld + 128u * (fl - row * G) + 8u * c;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (lds_void *)&stage[w][64 * i], 16, 0, 0);
+      }
+    }
+  };
+  // this lane's operand in step t: group j, chunk 2t + h, at byte
+  // 16 (64 (j / 4) + 16 (j % 4) + ((2t + h) ^ (j % 16))) = rd ^ 32t
+  const uint32_t rd = 1024u * (j >> 2) + 256u * (j & 3u) + 16u * (h ^ (j & 15u));
+  float lmax = 0.0f, araw = 0.0f;
+  QuadOut q;
+  uint32_t gbq = 0u;
+  bool actq = false;
+  uint32_t T = __builtin_amdgcn_readfirstlane(blockIdx.x * (kMxThreads / kWave) + (threadIdx.x >> 6));
+  if (T < ntiles) load_tile(T);
+  for (; T < ntiles; T += waves) {
+    // the staged tile (direct-to-LDS loads count in vmcnt only; earlier
+    // stores were issued before these loads)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    uint4 xb[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      xb[t] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(&stage[w][0]) + (rd ^ (32u * t)));
+    if constexpr (RAW) {
+      uint32_t wd[32];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        wd[4 * t] = xb[t].x;
+        wd[4 * t + 1] = xb[t].y;
+        wd[4 * t + 2] = xb[t].z;
+        wd[4 * t + 3] = xb[t].w;
+      }
+      araw = fmaxf(araw, raw_absmax<1>(wd));
+    }
+    f32x16_t acc[4];
+    mx_rotate(fr, xb, lane, acc);
+    mx_store<MODE>(q, gbq, actq, p);  // the previous tile's outputs
+    // the operands are in registers (the MFMAs have read them): the stage
+    // takes the next tile
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (T + waves < ntiles) load_tile(T + waves);
+    const uint32_t f = 32u * T + j;
+    gbq = 8u * f + 4u * h;
+    actq = f < nf;
+    mx_code4<MODE>(acc, gbq, actq, p, s_t, lmax, q);
+  }
+  mx_store<MODE>(q, gbq, actq, p);
+  if constexpr (writes_partials(MODE)) {
+    const float m = block_max(lmax, red, kMxThreads);
+    if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
+  }
+  if constexpr (RAW) raw_partial<kMxThreads>(p, araw, red);
 }
 
 // ---------------------------------------------------------------- axis 1
@@ -810,11 +1107,15 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
 }
 
 // ---------------------------------------------------------------- launch
+// bf16 input with the rotation: the matrix-core kernels (axis 0).
+static bool use_mx(const QuantParams &p, int in_bf16, int axis) { return in_bf16 && p.rht && axis == 0; }
+
 uint32_t quant_grid(const QuantParams &p, int in_bf16, int axis) {
-  (void)in_bf16;
   const uint64_t waves = kThreads / kWave;
-  uint64_t units = axis == 0 ? ((uint64_t)p.nblocks + kThreads - 1) / kThreads
-                             : ((uint64_t)p.ntiles + waves - 1) / waves;
+  const uint64_t mx_tiles = ((uint64_t)p.R * (p.K16 / 8) + 31) / 32;  // 32 groups
+  uint64_t units = use_mx(p, in_bf16, axis) ? (mx_tiles + kMxThreads / kWave - 1) / (kMxThreads / kWave)
+                   : axis == 0             ? ((uint64_t)p.nblocks + kThreads - 1) / kThreads
+                                           : ((uint64_t)p.ntiles + waves - 1) / waves;
   if (units < 1) units = 1;
   return (uint32_t)(units < (uint64_t)kMaxPartials ? units : kMaxPartials);
 }
@@ -826,12 +1127,14 @@ uint32_t eden_scales_grid(const QuantParams &p) {
   return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);
 }
 
-template <int IN_BF16, int MODE>
+template <int IN_BF16, int MODE, int RAW = 0>
 static void launch_one(const QuantParams &p, int axis, uint32_t grid, hipStream_t s) {
-  if (axis == 0)
-    hipLaunchKernelGGL((k_quant_rows<IN_BF16, MODE>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (use_mx(p, IN_BF16, axis))
+    hipLaunchKernelGGL((k_quant_rows_mx<MODE, RAW>), dim3(grid), dim3(kMxThreads), 0, s, p);
+  else if (axis == 0)
+    hipLaunchKernelGGL((k_quant_rows<IN_BF16, MODE, RAW>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((k_quant_cols<IN_BF16, MODE>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((k_quant_cols<IN_BF16, MODE, RAW>), dim3(grid), dim3(kThreads), 0, s, p);
 }
 
 template <int IN_BF16>
@@ -842,14 +1145,8 @@ static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid
     case kSr: launch_one<IN_BF16, kSr>(p, axis, grid, s); break;
     case kIf4: launch_one<IN_BF16, kIf4>(p, axis, grid, s); break;
     case kEden:
-      if (p.amax_out) {
-        if (axis == 0)
-          hipLaunchKernelGGL((k_quant_rows<IN_BF16, kEden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
-        else
-          hipLaunchKernelGGL((k_quant_cols<IN_BF16, kEden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
-      } else {
-        launch_one<IN_BF16, kEden>(p, axis, grid, s);
-      }
+      if (p.amax_out) launch_one<IN_BF16, kEden, 1>(p, axis, grid, s);
+      else launch_one<IN_BF16, kEden>(p, axis, grid, s);
       break;
     case kEdenFused: launch_one<IN_BF16, kEdenFused>(p, axis, grid, s); break;
     case kRot: launch_one<IN_BF16, kRot>(p, axis, grid, s); break;
@@ -857,14 +1154,8 @@ static void launch_mode(const QuantParams &p, int axis, Mode mode, uint32_t grid
     case kSearch: launch_one<IN_BF16, kSearch>(p, axis, grid, s); break;
     case kIf4Sr: launch_one<IN_BF16, kIf4Sr>(p, axis, grid, s); break;
     case kIf4Eden:
-      if (p.amax_out) {
-        if (axis == 0)
-          hipLaunchKernelGGL((k_quant_rows<IN_BF16, kIf4Eden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
-        else
-          hipLaunchKernelGGL((k_quant_cols<IN_BF16, kIf4Eden, 1>), dim3(grid), dim3(kThreads), 0, s, p);
-      } else {
-        launch_one<IN_BF16, kIf4Eden>(p, axis, grid, s);
-      }
+      if (p.amax_out) launch_one<IN_BF16, kIf4Eden, 1>(p, axis, grid, s);
+      else launch_one<IN_BF16, kIf4Eden>(p, axis, grid, s);
       break;
     case kIf4EdenFused: launch_one<IN_BF16, kIf4EdenFused>(p, axis, grid, s); break;
   }

@@ -2,9 +2,11 @@
 called through the C ABI (the Python binding marshals arguments only).
 
 Rotation off: packed codes, scales and the tensor scale are bit-exact.
-Rotation on: the kernels run the transform's stages in the oracle's order, so
-they are bit-exact too in practice; the assertion is the contract's
-(<= 1e-5 of codes one level apart, rotated values within 1e-5 relative).
+Rotation on: the contract's tolerance (<= 1e-5 of codes one level apart,
+rotated values within 1e-5 of their group's largest magnitude).  The
+butterfly kernels (fp32 input, columns) run the transform's stages in the
+oracle's order and are bit-exact in practice; bf16 rows rotate on the matrix
+cores, which round the same exact products' sums in another order.
 Sizes span several workgroups and a ragged tail.
 """
 import numpy as np
@@ -12,7 +14,7 @@ import pytest
 
 import oracle
 from nvfp4_bit_block_amd import synth
-from gpu_util import assert_bit_exact, assert_rotated_close, q_to_host, to_device
+from gpu_util import assert_bit_exact, assert_rotated_close, assert_rotation_values_close, q_to_host, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -196,7 +198,11 @@ def test_dual_axis_mseden(nv, dtype, group, rot):
                 assert_bit_exact(g, ref, what)
             sep = q_to_host(nv.quantize_nvfp4(xt, rounding="mseden", axis=axis, rht_signs=signs, seed=3,
                                               stream_id=2, eden_group=group))
-            assert_bit_exact(g, sep, what + " vs separate call")
+            if rot and dtype == "bf16" and axis == 0:
+                # the separate row call rotates on the matrix cores
+                assert_rotated_close(g, sep, what=what + " vs separate call")
+            else:
+                assert_bit_exact(g, sep, what + " vs separate call")
 
 
 def test_dual_axis_given_scale(nv):
@@ -210,41 +216,55 @@ def test_dual_axis_given_scale(nv):
         assert_bit_exact(q_to_host(q), ref, f"dual given scale axis{axis}")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("axis", [0, 1])
-def test_rht_values(nv, axis):
+def test_rht_values(nv, axis, dtype):
+    """fp32 input: the butterfly stages in the oracle's order, bit-exact
+    (signed zeros included); bf16 input along rows: the matrix-core product,
+    within the rotation tolerance of each group's largest value."""
     import torch
     rng = np.random.default_rng(8)
     signs = synth.signs_from_rng(rng)
     x = synth.gradient(256, 384, seed=9)[0]
-    z = nv.rht(to_device(x, "bf16"), signs, axis=axis).cpu().numpy()
+    z = nv.rht(to_device(x, dtype), signs, axis=axis).cpu().numpy()
     view = x if axis == 0 else np.ascontiguousarray(x.T)
     ref = oracle.rht(view, oracle.signs_words(signs))
-    rel = np.abs(z - ref) / np.maximum(np.abs(ref), 1e-30)
-    assert np.max(np.abs(z - ref) / (np.abs(ref).max())) <= 1e-5
-    assert np.mean(rel > 1e-5) <= 1e-5
-    # the kernels run the butterfly stages in the oracle's order: bit-exact,
-    # signed zeros included (exact cancellations occur on bf16 inputs)
-    assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
+    assert_rotation_values_close(z, ref, what=f"rotation {dtype} axis{axis}")
+    if dtype == "fp32" or axis == 1:
+        assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
+    else:
+        # both round sums of the same exact products: far inside the tolerance
+        assert_rotation_values_close(z, ref, tol=1e-6, what=f"rotation {dtype} axis{axis}")
     torch.cuda.synchronize()
 
 
-def test_rht_signed_zero_cancellations(nv):
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rht_signed_zero_cancellations(nv, dtype):
     """Inputs whose rotated values cancel to exactly zero in many butterflies:
-    the sign of every zero matches the oracle."""
+    the butterfly kernels (fp32 input, and the columns) match the oracle bit
+    for bit, the sign of every zero included; the matrix-core rows (bf16)
+    match it as values (a zero of either sign)."""
     rng = np.random.default_rng(21)
     signs = synth.signs_from_rng(rng)
     x = np.repeat(rng.choice(np.array([1.0, -1.0, 0.5, 0.0], dtype=np.float32), (64, 8)), 16, axis=1)
     x[:, ::3] *= -1
     for axis in (0, 1):
+        exact = dtype == "fp32" or axis == 1
         xin = x if axis == 0 else np.ascontiguousarray(x.T)
-        z = nv.rht(to_device(xin, "bf16"), signs, axis=axis).cpu().numpy()
+        z = nv.rht(to_device(xin, dtype), signs, axis=axis).cpu().numpy()
         ref = oracle.rht(x, oracle.signs_words(signs))
         assert np.count_nonzero(ref == 0) > 100
-        assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
+        if exact:
+            assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
+        else:
+            assert np.array_equal(z, ref)  # values; -0 == +0
         for rnd, name in ((oracle.RTN, "rtn"), (oracle.MSEDEN, "mseden")):
-            g = q_to_host(nv.quantize_nvfp4(to_device(xin, "bf16"), rounding=name, axis=axis, rht_signs=signs))
+            g = q_to_host(nv.quantize_nvfp4(to_device(xin, dtype), rounding=name, axis=axis, rht_signs=signs))
             r = oracle.quantize(xin, rounding=rnd, axis=axis, rht_on=True, signs_w=oracle.signs_words(signs))
-            assert_bit_exact(g, r, f"zero cancellations {name} axis{axis}")
+            if exact:
+                assert_bit_exact(g, r, f"zero cancellations {name} {dtype} axis{axis}")
+            else:
+                assert_rotated_close(g, r, frac=0.0, what=f"zero cancellations {name} {dtype} axis{axis}")
 
 
 def _negative_zero_groups(signs, rows, cols, seed):
@@ -274,10 +294,13 @@ def _negative_zero_groups(signs, rows, cols, seed):
     return x
 
 
-def test_rotation_negative_zero_outputs(nv):
-    """Rotated outputs that are -0 in the oracle come out -0 on the GPU too,
-    while other groups of the same waves take the fast stages: rotation
-    values, RTN, SR and MS-EDEN codes, rows, columns and both axes at once."""
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rotation_negative_zero_outputs(nv, dtype):
+    """Rotated outputs that are -0 in the oracle: the butterfly kernels (fp32
+    input, columns, both axes at once) give -0 too, while other groups of the
+    same waves take the fast stages -- rotation values, RTN, SR and MS-EDEN
+    codes; the matrix-core rows (bf16) give the same values, a zero of either
+    sign."""
     import torch
     rng = np.random.default_rng(34)
     signs = synth.signs_from_rng(rng)
@@ -287,19 +310,27 @@ def test_rotation_negative_zero_outputs(nv):
     assert np.count_nonzero((ref_rot == 0) & np.signbit(ref_rot)) > 50
     assert np.count_nonzero((ref_rot == 0) & ~np.signbit(ref_rot)) > 50
     for axis in (0, 1):
+        exact = dtype == "fp32" or axis == 1
         xin = x if axis == 0 else np.ascontiguousarray(x.T)
-        z = nv.rht(to_device(xin, "bf16"), signs, axis=axis).cpu().numpy()
-        assert np.array_equal(z.view(np.uint32), ref_rot.view(np.uint32)), f"rotation axis{axis}"
+        z = nv.rht(to_device(xin, dtype), signs, axis=axis).cpu().numpy()
+        if exact:
+            assert np.array_equal(z.view(np.uint32), ref_rot.view(np.uint32)), f"rotation axis{axis}"
+        else:
+            assert_rotation_values_close(z, ref_rot, tol=1e-6, what=f"rotation axis{axis}")
+            assert np.all(z[ref_rot == 0] == 0), f"rotation axis{axis}: exact zeros"
         for name, rnd in (("rtn", oracle.RTN), ("sr", oracle.SR), ("mseden", oracle.MSEDEN)):
-            g = q_to_host(nv.quantize_nvfp4(to_device(xin, "bf16"), rounding=name, axis=axis, rht_signs=signs,
+            g = q_to_host(nv.quantize_nvfp4(to_device(xin, dtype), rounding=name, axis=axis, rht_signs=signs,
                                             seed=6, stream_id=2))
             r = oracle.quantize(xin, rounding=rnd, axis=axis, rht_on=True, signs_w=w, seed=6, stream=2)
-            assert_bit_exact(g, r, f"-0 outputs {name} axis{axis}")
+            if exact:
+                assert_bit_exact(g, r, f"-0 outputs {name} {dtype} axis{axis}")
+            else:
+                assert_rotated_close(g, r, frac=0.0, what=f"-0 outputs {name} {dtype} axis{axis}")
     xt = x.T.copy()        # both axes at once quantize along the rows of their input
-    qr, qc = nv.quantize_nvfp4_dual(to_device(xt, "bf16"), rht_signs=signs, seed=8)
+    qr, qc = nv.quantize_nvfp4_dual(to_device(xt, dtype), rht_signs=signs, seed=8)
     for axis, q in ((0, qr), (1, qc)):
         r = oracle.quantize(xt, rounding=oracle.MSEDEN, axis=axis, rht_on=True, signs_w=w, seed=8)
-        assert_bit_exact(q_to_host(q), r, f"-0 outputs dual axis{axis}")
+        assert_bit_exact(q_to_host(q), r, f"-0 outputs dual {dtype} axis{axis}")
     torch.cuda.synchronize()
 
 

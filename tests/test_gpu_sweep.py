@@ -2,7 +2,7 @@
 axis, rounding and format, scale rule, rotation, a given tensor scale,
 ragged shapes and value distributions (Gaussian, heavy-tailed, sparse with
 exact zeros, tiny and huge magnitudes).  Rotation off: bit-exact; rotation
-on: the rotation contract (which the kernels in fact meet bit-exactly).
+on: the rotation contract.
 Followed by random GEMM shapes on the swept operands."""
 import numpy as np
 import pytest
