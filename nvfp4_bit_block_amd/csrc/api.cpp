@@ -144,6 +144,9 @@ void fill_common(QuantParams &p, const void *x, int in_dtype, int64_t rows, int6
   const uint32_t ntt = (uint32_t)((rows + 127) / 128);
   p.ctiles_div = make_fastdiv(nct ? nct : 1);
   p.ntiles = nct * ntt;
+  const uint32_t mx_nct = (uint32_t)((cols + 63) / 64), mx_npair = (uint32_t)((rows + 255) / 256);
+  p.mx_cdiv = make_fastdiv(mx_nct ? mx_nct : 1);
+  p.mx_rdiv = make_fastdiv(mx_npair ? mx_npair : 1);
   p.codes = codes;
   p.scales = scales;
   p.ts_out = tensor_scale;

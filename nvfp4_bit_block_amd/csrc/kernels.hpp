@@ -52,6 +52,8 @@ struct QuantParams {
   FastDiv k16div;       // division by K16 (axis 0)
   FastDiv ctiles_div;   // division by the number of column tiles (axis 1)
   uint32_t ntiles;      // axis 1 tile count
+  FastDiv mx_cdiv;      // axis 1, matrix-core rotation: division by the 64-column tiles
+  FastDiv mx_rdiv;      // ... by the 256-row tiles
   uint8_t *codes;
   uint8_t *scales;
   float *ts_out;

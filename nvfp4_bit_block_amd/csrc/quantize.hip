@@ -832,6 +832,127 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_rows_mx(QuantParams p) {
   if constexpr (RAW) raw_partial<kMxThreads>(p, araw, red);
 }
 
+// Axis 1, bf16 input (rows 16-byte aligned), rotation on.  A workgroup tile
+// is two 128-row groups of 64 columns (256 rows x 128 bytes, 32 KB), staged
+// in LDS by direct-to-LDS loads: wave w loads rows 64w .. 64w+63, load i
+// rows 64w + 8i .. +7 (1 KB, coalesced); lane l of it takes 16-byte chunk
+// (l % 8) ^ f(row) of its row, f(r) = 2 ((r / 2) % 2) + 4 (r / 128), landing
+// at slot 8 row + l % 8.  Wave w then rotates columns 16w .. 16w+15 of both
+// groups: lane (j, h) takes column 16w + j % 16 of group j / 16, so that its
+// column's 128 bytes of codes per tile are in 4 lanes of one store.  Its
+// operand in step t is the 8 elements at rows in(t, h, e) =
+// 16t + 8 (e / 4) + 4h + e % 4 of its group: two transposing reads
+// (ds_read_b64_tr_b16: in a group of 16 lanes, lane i receives element i % 4
+// of the 8-byte vectors that lanes 4q + i / 4 point at, q = 0..3), each lane
+// pointing at 4 columns of one of 4 rows; the swizzle puts the 8 rows that
+// 32 lanes read on disjoint LDS banks.  Lane (j, h) codes blocks 4h .. 4h+3.
+// Columns past the last read what follows in memory, rows past the last
+// zeros (the buffer's range check at the tensor's end); neither is stored.
+// RAW as for k_quant_cols.
+template <int MODE, int RAW = 0>
+__global__ __launch_bounds__(kMxThreads) void k_quant_cols_mx(QuantParams p) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  static_assert(kMxThreads == 256, "four waves of 16 columns");
+  __shared__ RotFrags fr;
+  __shared__ uint4 stage[2048];  // 256 rows x 8 chunks
+  // (the reductions before and after the loop use the stage's first bytes)
+  float *const red = reinterpret_cast<float *>(&stage[0]);
+  float s_t = 1.0f;
+  if constexpr (takes_tensor_scale(MODE)) {
+    s_t = tensor_scale<kMxThreads>(p, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  }
+  mx_build_frags<1>(p.sg, fr);
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63u, j = lane & 31u, h = lane >> 5;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t ngroups = p.rows >> 7;
+  const uint32_t npair = p.mx_rdiv.d, nct = p.mx_cdiv.d;  // 256-row tiles, 64-column tiles
+  const uint32_t ntiles = npair * nct;
+  // Tile order: row pair fastest, so that consecutive tiles code the next
+  // 128 bytes of the same output rows; each XCD (workgroups go round-robin to
+  // the 8 XCDs: the grid is a multiple of 8) takes a contiguous eighth of the
+  // tiles.
+  const uint32_t xcd = blockIdx.x & 7u, per = (ntiles + 7u) >> 3;
+  const uint32_t first = xcd * per, last = min(first + per, ntiles);
+  const uint32_t step = gridDim.x >> 3;
+  const uint32_t row_bytes = (uint32_t)p.ld * 2u;  // 256 rows of it fit in 31 bits (launch condition)
+  const uint64_t end = ((uint64_t)(p.rows - 1u) * (uint64_t)p.ld + p.cols) * 2u;
+  // load i, lane l: row 64w + 8i + l / 8, chunk (l % 8) ^ f(row)
+  const uint32_t voff = (64u * w + (lane >> 3)) * row_bytes +
+                        16u * ((lane & 7u) ^ (2u * ((lane >> 4) & 1u) + 4u * (w >> 1)));
+  auto load_tile = [&](uint32_t T) {
+    const uint32_t cb = fdiv(T, p.mx_rdiv), tp = T - cb * npair;
+    const uint64_t base = (uint64_t)tp * 256u * row_bytes + 128u * cb;
+    const uint64_t left = end > base ? end - base : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint8_t *>(p.x) + base), (short)0,
+        (int)(left < 0x7FFFFFFFull ? left : 0x7FFFFFFFull), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&stage[64u * (8u * w + i)], 16,
+                                               voff + 8u * i * row_bytes, 0, 0, 0);
+  };
+  // transposing reads: lane (G = l / 16, s = l % 16) of group g = G % 2, half
+  // h = G / 2 points at row 128g + 16t + 8 e2 + 4h + s / 4, columns
+  // 16w + 4 (s % 4) .. +3 (e2 = 0, 1: elements 0..3 and 4..7 of the
+  // operand), at byte rdb + 2048 t + 1024 e2
+  const uint32_t sl = lane & 15u, gg = (lane >> 4) & 1u;
+  const uint32_t rdb = 128u * (128u * gg + 4u * h + (sl >> 2)) +
+                       16u * ((2u * w + ((sl & 3u) >> 1)) ^ (2u * ((sl >> 3) & 1u) + 4u * gg)) + 8u * (sl & 1u);
+  const uint8_t *const st8 = reinterpret_cast<const uint8_t *>(&stage[0]);
+  float lmax = 0.0f, araw = 0.0f;
+  QuadOut q;
+  uint32_t gbq = 0u;
+  bool actq = false;
+  uint32_t T = first + (blockIdx.x >> 3);
+  if (T < last) load_tile(T);
+  for (; T < last; T += step) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the tile
+    __builtin_amdgcn_s_barrier();        // ... and every wave's
+    uint4 xb[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st8 + rdb + 2048u * t));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(st8 + rdb + 2048u * t + 1024u));
+      const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+      xb[t] = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the operands are in registers
+    __builtin_amdgcn_s_barrier();        // every wave's: the stage is free
+    const uint32_t cb = fdiv(T, p.mx_rdiv), tp = T - cb * npair;
+    const uint32_t col = 64u * cb + 16u * w + (j & 15u), grp = 2u * tp + (j >> 4);
+    const bool act = col < p.cols && grp < ngroups;
+    if constexpr (RAW) {
+      uint32_t wd[32];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        wd[4 * t] = xb[t].x;
+        wd[4 * t + 1] = xb[t].y;
+        wd[4 * t + 2] = xb[t].z;
+        wd[4 * t + 3] = xb[t].w;
+      }
+      // (columns past the last hold other data: masked)
+      if (act) araw = fmaxf(araw, raw_absmax<1>(wd));
+    }
+    mx_store<MODE>(q, gbq, actq, p);  // the previous tile's outputs
+    if (T + step < last) load_tile(T + step);
+    f32x16_t acc[4];
+    mx_rotate(fr, xb, lane, acc);
+    gbq = col * p.K16 + 8u * grp + 4u * h;
+    actq = act;
+    mx_code4<MODE>(acc, gbq, actq, p, s_t, lmax, q);
+  }
+  mx_store<MODE>(q, gbq, actq, p);
+  if constexpr (writes_partials(MODE)) {
+    const float m = block_max(lmax, red, kMxThreads);
+    if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
+  }
+  if constexpr (RAW) raw_partial<kMxThreads>(p, araw, red);
+}
+
 // ---------------------------------------------------------------- axis 1
 // A wave's tile is 128 positions along the reduction (input rows) x 128 bytes
 // of columns (64 bf16 or 32 fp32 columns).  Lane (q = lane bits 2, 4, 5;
@@ -1107,13 +1228,19 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
 }
 
 // ---------------------------------------------------------------- launch
-// bf16 input with the rotation: the matrix-core kernels (axis 0).
-static bool use_mx(const QuantParams &p, int in_bf16, int axis) { return in_bf16 && p.rht && axis == 0; }
+// bf16 input with the rotation: the matrix-core kernels (axis 1: rows
+// 16-byte aligned, 256 of them within 2^31 bytes).
+static bool use_mx(const QuantParams &p, int in_bf16, int axis) {
+  return in_bf16 && p.rht && (axis == 0 || (p.vec && (uint64_t)p.ld * 2u * 256u <= 0x7FFFFFFFull));
+}
 
 uint32_t quant_grid(const QuantParams &p, int in_bf16, int axis) {
   const uint64_t waves = kThreads / kWave;
-  const uint64_t mx_tiles = ((uint64_t)p.R * (p.K16 / 8) + 31) / 32;  // 32 groups
-  uint64_t units = use_mx(p, in_bf16, axis) ? (mx_tiles + kMxThreads / kWave - 1) / (kMxThreads / kWave)
+  // matrix-core rotation: axis 0, a wave per 32 groups; axis 1, a workgroup
+  // per 128 rows x 128 columns
+  const uint64_t mx_units = axis == 0 ? (((uint64_t)p.R * (p.K16 / 8) + 31) / 32 + waves - 1) / waves
+                                      : ((uint64_t)p.mx_rdiv.d * p.mx_cdiv.d + 7) / 8 * 8;
+  uint64_t units = use_mx(p, in_bf16, axis) ? mx_units
                    : axis == 0             ? ((uint64_t)p.nblocks + kThreads - 1) / kThreads
                                            : ((uint64_t)p.ntiles + waves - 1) / waves;
   if (units < 1) units = 1;
@@ -1129,8 +1256,10 @@ uint32_t eden_scales_grid(const QuantParams &p) {
 
 template <int IN_BF16, int MODE, int RAW = 0>
 static void launch_one(const QuantParams &p, int axis, uint32_t grid, hipStream_t s) {
-  if (use_mx(p, IN_BF16, axis))
+  if (use_mx(p, IN_BF16, axis) && axis == 0)
     hipLaunchKernelGGL((k_quant_rows_mx<MODE, RAW>), dim3(grid), dim3(kMxThreads), 0, s, p);
+  else if (use_mx(p, IN_BF16, axis))
+    hipLaunchKernelGGL((k_quant_cols_mx<MODE, RAW>), dim3(grid), dim3(kMxThreads), 0, s, p);
   else if (axis == 0)
     hipLaunchKernelGGL((k_quant_rows<IN_BF16, MODE, RAW>), dim3(grid), dim3(kThreads), 0, s, p);
   else

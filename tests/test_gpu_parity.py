@@ -4,9 +4,10 @@ called through the C ABI (the Python binding marshals arguments only).
 Rotation off: packed codes, scales and the tensor scale are bit-exact.
 Rotation on: the contract's tolerance (<= 1e-5 of codes one level apart,
 rotated values within 1e-5 of their group's largest magnitude).  The
-butterfly kernels (fp32 input, columns) run the transform's stages in the
-oracle's order and are bit-exact in practice; bf16 rows rotate on the matrix
-cores, which round the same exact products' sums in another order.
+butterfly kernels (fp32 input; both axes at once) run the transform's stages
+in the oracle's order and are bit-exact in practice; bf16 input rotates on
+the matrix cores, which round the same exact products' sums in another
+order.
 Sizes span several workgroups and a ragged tail.
 """
 import numpy as np
@@ -198,8 +199,8 @@ def test_dual_axis_mseden(nv, dtype, group, rot):
                 assert_bit_exact(g, ref, what)
             sep = q_to_host(nv.quantize_nvfp4(xt, rounding="mseden", axis=axis, rht_signs=signs, seed=3,
                                               stream_id=2, eden_group=group))
-            if rot and dtype == "bf16" and axis == 0:
-                # the separate row call rotates on the matrix cores
+            if rot and dtype == "bf16":
+                # the separate calls rotate on the matrix cores
                 assert_rotated_close(g, sep, what=what + " vs separate call")
             else:
                 assert_bit_exact(g, sep, what + " vs separate call")
@@ -220,8 +221,8 @@ def test_dual_axis_given_scale(nv):
 @pytest.mark.parametrize("axis", [0, 1])
 def test_rht_values(nv, axis, dtype):
     """fp32 input: the butterfly stages in the oracle's order, bit-exact
-    (signed zeros included); bf16 input along rows: the matrix-core product,
-    within the rotation tolerance of each group's largest value."""
+    (signed zeros included); bf16 input: the matrix-core product, within the
+    rotation tolerance of each group's largest value."""
     import torch
     rng = np.random.default_rng(8)
     signs = synth.signs_from_rng(rng)
@@ -230,7 +231,7 @@ def test_rht_values(nv, axis, dtype):
     view = x if axis == 0 else np.ascontiguousarray(x.T)
     ref = oracle.rht(view, oracle.signs_words(signs))
     assert_rotation_values_close(z, ref, what=f"rotation {dtype} axis{axis}")
-    if dtype == "fp32" or axis == 1:
+    if dtype == "fp32":
         assert np.array_equal(z.view(np.uint32), ref.view(np.uint32))
     else:
         # both round sums of the same exact products: far inside the tolerance
@@ -241,15 +242,15 @@ def test_rht_values(nv, axis, dtype):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_rht_signed_zero_cancellations(nv, dtype):
     """Inputs whose rotated values cancel to exactly zero in many butterflies:
-    the butterfly kernels (fp32 input, and the columns) match the oracle bit
-    for bit, the sign of every zero included; the matrix-core rows (bf16)
-    match it as values (a zero of either sign)."""
+    the butterfly kernels (fp32 input) match the oracle bit for bit, the sign
+    of every zero included; the matrix-core kernels (bf16) match it as values
+    (a zero of either sign)."""
     rng = np.random.default_rng(21)
     signs = synth.signs_from_rng(rng)
     x = np.repeat(rng.choice(np.array([1.0, -1.0, 0.5, 0.0], dtype=np.float32), (64, 8)), 16, axis=1)
     x[:, ::3] *= -1
     for axis in (0, 1):
-        exact = dtype == "fp32" or axis == 1
+        exact = dtype == "fp32"
         xin = x if axis == 0 else np.ascontiguousarray(x.T)
         z = nv.rht(to_device(xin, dtype), signs, axis=axis).cpu().numpy()
         ref = oracle.rht(x, oracle.signs_words(signs))
@@ -297,9 +298,9 @@ def _negative_zero_groups(signs, rows, cols, seed):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_rotation_negative_zero_outputs(nv, dtype):
     """Rotated outputs that are -0 in the oracle: the butterfly kernels (fp32
-    input, columns, both axes at once) give -0 too, while other groups of the
-    same waves take the fast stages -- rotation values, RTN, SR and MS-EDEN
-    codes; the matrix-core rows (bf16) give the same values, a zero of either
+    input, both axes at once) give -0 too, while other groups of the same
+    waves take the fast stages -- rotation values, RTN, SR and MS-EDEN codes;
+    the matrix-core kernels (bf16) give the same values, a zero of either
     sign."""
     import torch
     rng = np.random.default_rng(34)
@@ -310,7 +311,7 @@ def test_rotation_negative_zero_outputs(nv, dtype):
     assert np.count_nonzero((ref_rot == 0) & np.signbit(ref_rot)) > 50
     assert np.count_nonzero((ref_rot == 0) & ~np.signbit(ref_rot)) > 50
     for axis in (0, 1):
-        exact = dtype == "fp32" or axis == 1
+        exact = dtype == "fp32"
         xin = x if axis == 0 else np.ascontiguousarray(x.T)
         z = nv.rht(to_device(xin, dtype), signs, axis=axis).cpu().numpy()
         if exact:
