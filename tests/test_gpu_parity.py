@@ -424,7 +424,40 @@ def test_columns_unaligned_rows_and_many_tiles(nv, dtype):
     for name, rnd in (("rtn", oracle.RTN), ("mseden", oracle.MSEDEN)):
         g = q_to_host(nv.quantize_nvfp4(to_device(y, dtype), rounding=name, axis=1, rht_signs=signs, seed=5))
         r = oracle.quantize(y, rounding=rnd, axis=1, rht_on=True, signs_w=oracle.signs_words(signs), seed=5)
-        assert_bit_exact(g, r, f"many tiles {name} {dtype}")
+        if dtype == "bf16":  # the matrix-core rotation
+            assert_rotated_close(g, r, what=f"many tiles {name} {dtype}")
+        else:
+            assert_bit_exact(g, r, f"many tiles {name} {dtype}")
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_matrix_core_rotation_layouts(nv, axis):
+    """The matrix-core rotation (bf16) on layouts its tiling treats apart:
+    strided views (axis 0: per-group addresses instead of one contiguous
+    tile; axis 1: a leading dimension above the row length), a last tile with
+    one 128-row group of two and a ragged column tile (axis 1), a group count
+    that leaves the last 32-group tile partial (axis 0), and a view offset by
+    8 (axis 0) or 4 (axis 1: rows not 16-byte aligned, the butterfly kernel
+    instead) elements."""
+    import torch
+    rng = np.random.default_rng(47)
+    signs = synth.signs_from_rng(rng)
+    w = oracle.signs_words(signs)
+    x = synth.gradient(384, 840, seed=48)[0]
+    full = torch.from_numpy(x).to(torch.bfloat16).to("cuda:0")
+    cases = [("dense", x[:-1, :640] if axis == 0 else x[:, :200], None),
+             ("strided", x[:, 64:576], (64, 576)),
+             ("unaligned", x[:, 4:516] if axis == 1 else x[:, 8:520], (4, 516) if axis == 1 else (8, 520))]
+    for name, xv, cut in cases:
+        xv = np.ascontiguousarray(xv)
+        t = to_device(xv, "bf16") if cut is None else full[:, cut[0]:cut[1]]
+        for rn, rnd in (("rtn", oracle.RTN), ("sr", oracle.SR), ("mseden", oracle.MSEDEN)):
+            g = q_to_host(nv.quantize_nvfp4(t, rounding=rn, axis=axis, rht_signs=signs, seed=2, stream_id=1))
+            r = oracle.quantize(xv, rounding=rnd, axis=axis, rht_on=True, signs_w=w, seed=2, stream=1)
+            assert_rotated_close(g, r, what=f"{name} {rn} axis{axis} {xv.shape}")
+        z = nv.rht(t, signs, axis=axis).cpu().numpy()
+        assert_rotation_values_close(z, oracle.rht(xv if axis == 0 else np.ascontiguousarray(xv.T), w),
+                                     what=f"{name} rotation axis{axis}")
 
 
 def test_strided_input(nv):
