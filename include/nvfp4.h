@@ -343,7 +343,12 @@ int nvfp4_gemm_nvfp4_rtn(const uint8_t *a_codes, const uint8_t *a_scales, const 
  * micro-scaling groups before MS-EDEN); PAL opening paragraph (a random
  * sign flip followed by a Hadamard transform)], for checking it:
  * out[rows_out x K] fp32 = the rotated values of step 1 of
- * nvfp4_quantize_nvfp4, in the output layout of `axis`.
+ * nvfp4_quantize_nvfp4, in the output layout of `axis`: for bf16 input the
+ * product with the +-1 matrix H diag(signs) on the matrix cores (exact
+ * products, fp32 sums), for fp32 input (and bf16 columns whose rows are not
+ * 16-byte aligned) the butterfly stages in Sylvester order; then times
+ * fp32(1/sqrt(128)).  The two evaluations of the same sums agree to fp32
+ * rounding of the partial sums.
  * Same x rules; K % 128 == 0; out device, 16-byte aligned.
  */
 int nvfp4_rht(const void *x, int in_dtype, int64_t rows, int64_t cols, int64_t ld, int axis,
