@@ -1167,6 +1167,136 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
   }
 }
 
+// Both axes at once, bf16 input (rows 16-byte aligned), rotation on.  A
+// workgroup tile is 128 rows x 128 columns: one group along each axis
+// (32 KB), staged in LDS by direct-to-LDS loads from one read of the input:
+// wave w loads rows 32w .. 32w+31, load i rows 32w + 4i .. +3 (1 KB); lane l
+// of it takes 16-byte chunk (l % 16) ^ f(row), f(r) = 4 (r % 4) + (r / 4) % 4,
+// landing at slot 16 row + l % 16.  Then wave w rotates rows 32w .. 32w+31
+// (lane (j, h): two 8-byte reads per step of row 32w + j, at positions
+// in(t, h, e) = 16t + 8 (e / 4) + 4h + e % 4) and columns 32w .. 32w+31
+// (lane (j, h): two transposing reads per step, as in k_quant_cols_mx), with
+// the same fragments.  f spreads the 4 rows of a transposing read over 4
+// different 64-byte bank groups, and the 32 rows of a row read over 16
+// chunk positions (two rows per bank group).  The row pass is coded first;
+// the next tile's loads are issued once the column operands are read too.  Tiles run with the
+// column block fastest, each XCD taking a contiguous share, so that a row's
+// successive 64-byte code runs are written by one L2.  pr / pc: the
+// row-wise (axis 0) and column-wise (axis 1) outputs.
+template <int MODE>
+__global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, QuantParams pc) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  static_assert(kMxThreads == 256, "four waves of 32 rows and 32 columns");
+  __shared__ RotFrags fr;
+  __shared__ uint4 stage[2048];  // 128 rows x 16 chunks
+  float *const red = reinterpret_cast<float *>(&stage[0]);
+  float s_r = 1.0f, s_c = 1.0f;
+  if constexpr (MODE == kEdenFused) {
+    s_r = *pr.ts_in;
+    s_c = *pc.ts_in;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *pr.ts_out = s_r;
+      *pc.ts_out = s_c;
+    }
+  }
+  mx_build_frags<1>(pr.sg, fr);
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63u, j = lane & 31u, h = lane >> 5;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t ncb = pr.K16 >> 3, nrb = pr.rows >> 7;  // 128-column blocks, 128-row blocks
+  const uint32_t ntiles = nrb * ncb;
+  const uint32_t xcd = blockIdx.x & 7u, per = (ntiles + 7u) >> 3;
+  const uint32_t first = xcd * per, last = min(first + per, ntiles);
+  const uint32_t step = gridDim.x >> 3;
+  const uint32_t row_bytes = (uint32_t)pr.ld * 2u;  // 128 rows of it fit in 31 bits (launch condition)
+  const uint64_t end = ((uint64_t)(pr.rows - 1u) * (uint64_t)pr.ld + pr.cols) * 2u;
+  auto swz = [](uint32_t r) { return 4u * (r & 3u) + ((r >> 2) & 3u); };
+  // load i, lane l: row 32w + 4i + l / 16, chunk (l % 16) ^ f(row)
+  uint32_t voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = 32u * w + 4u * i + (lane >> 4);
+    voff[i] = r * row_bytes + 16u * ((lane & 15u) ^ swz(r));
+  }
+  auto load_tile = [&](uint32_t T) {
+    const uint32_t rb = fdiv(8u * T, pr.k16div), cb = T - rb * ncb;
+    const uint64_t base = (uint64_t)rb * 128u * row_bytes + 256u * cb;
+    const uint64_t left = end > base ? end - base : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint8_t *>(pr.x) + base), (short)0,
+        (int)(left < 0x7FFFFFFFull ? left : 0x7FFFFFFFull), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&stage[64u * (8u * w + i)], 16, voff[i], 0, 0, 0);
+  };
+  const uint8_t *const st8 = reinterpret_cast<const uint8_t *>(&stage[0]);
+  // row reads: row rr = 32w + j, chunk (2t + e2) ^ f(rr), byte 8h
+  const uint32_t rr = 32u * w + j, fr_r = swz(rr);
+  // transposing reads: lane (G = l / 16, s = l % 16) points at row
+  // 16t + 8 e2 + 4 (G / 2) + s / 4 (f of which is 4 (s / 4) + e2... taken per
+  // read) and columns 32w + 16 (G % 2) + 4 (s % 4) .. +3
+  const uint32_t sl = lane & 15u, g16 = lane >> 4;
+  const uint32_t ccol = 32u * w + 16u * (g16 & 1u) + 4u * (sl & 3u);
+  float lmax_r = 0.0f, lmax_c = 0.0f;
+  uint32_t T = first + (blockIdx.x >> 3);
+  if (T < last) load_tile(T);
+  for (; T < last; T += step) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the tile
+    __builtin_amdgcn_s_barrier();        // ... and every wave's
+    const uint32_t rb = fdiv(8u * T, pr.k16div), cb = T - rb * ncb;
+    // rows first (operands, MFMAs, coding), then the column operands; the
+    // next tile's loads go out once both have been read
+    {
+      uint4 xr[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(st8 + 256u * rr + 16u * ((2u * t) ^ fr_r) + 8u * h);
+        const uint2 b = *reinterpret_cast<const uint2 *>(st8 + 256u * rr + 16u * ((2u * t + 1u) ^ fr_r) + 8u * h);
+        xr[t] = make_uint4(a.x, a.y, b.x, b.y);
+      }
+      f32x16_t acc[4];
+      mx_rotate(fr, xr, lane, acc);
+      QuadOut q;
+      const uint32_t gb0 = (128u * rb + rr) * pr.K16 + 8u * cb + 4u * h;
+      mx_code4<MODE>(acc, gb0, true, pr, s_r, lmax_r, q);
+      mx_store<MODE>(q, gb0, true, pr);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 xc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint2 v[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const uint32_t r = 16u * t + 8u * e2 + 4u * (g16 >> 1) + (sl >> 2);
+        const s16x4_t x4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(st8 + 256u * r + 16u * ((ccol >> 3) ^ swz(r)) + 2u * (ccol & 7u)));
+        v[e2] = __builtin_bit_cast(uint2, x4);
+      }
+      xc[t] = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the operands are in registers
+    __builtin_amdgcn_s_barrier();        // every wave's: the stage is free
+    if (T + step < last) load_tile(T + step);
+    {
+      f32x16_t acc[4];
+      mx_rotate(fr, xc, lane, acc);
+      QuadOut q;
+      const uint32_t gb0 = (128u * cb + 32u * w + j) * pc.K16 + 8u * rb + 4u * h;
+      mx_code4<MODE>(acc, gb0, true, pc, s_c, lmax_c, q);
+      mx_store<MODE>(q, gb0, true, pc);
+    }
+  }
+  if constexpr (MODE == kEden) {
+    const float mr = block_max(lmax_r, red, kMxThreads);
+    if (threadIdx.x == 0) pr.partial[blockIdx.x] = mr;
+    const float mc = block_max(lmax_c, red, kMxThreads);
+    if (threadIdx.x == 0) pc.partial[blockIdx.x] = mc;
+  }
+}
+
 // ---------------------------------------------------------------- MS-EDEN scales
 // Scale byte of a target t (sign bit: IF4's INT flag, bit 7 of the byte).
 __device__ __forceinline__ uint32_t eden_scale_byte(float t, const Divisor &s_t, uint32_t u16) {
@@ -1299,7 +1429,18 @@ hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, 
   return hipGetLastError();
 }
 
+// Both axes on the matrix cores: bf16 with the rotation, rows 16-byte
+// aligned, 128 of them within 2^31 bytes, whole 128-column blocks.
+static bool use_dual_mx(const QuantParams &pr, int in_bf16) {
+  return in_bf16 && pr.rht && pr.vec && pr.cols % 128 == 0 && (uint64_t)pr.ld * 2u * 128u <= 0x7FFFFFFFull;
+}
+
 uint32_t dual_grid(const QuantParams &pr, int in_bf16) {
+  if (use_dual_mx(pr, in_bf16)) {
+    const uint64_t tiles = (uint64_t)(pr.rows / 128) * (pr.cols / 128);
+    const uint64_t g = (tiles + 7) / 8 * 8;
+    return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);
+  }
   const uint32_t width = 4u * (in_bf16 ? ColCfg<1>::kTileCols : ColCfg<0>::kTileCols);
   const uint64_t tiles = (uint64_t)(pr.rows / 128) * ((pr.cols + width - 1) / width);
   uint64_t g = tiles < 1 ? 1 : tiles;
@@ -1308,7 +1449,10 @@ uint32_t dual_grid(const QuantParams &pr, int in_bf16) {
 
 hipError_t launch_quant_dual(const QuantParams &pr, const QuantParams &pc, int in_bf16, int fused,
                              uint32_t grid, hipStream_t s) {
-  if (in_bf16) {
+  if (use_dual_mx(pr, in_bf16)) {
+    if (fused) hipLaunchKernelGGL((k_quant_dual_mx<kEdenFused>), dim3(grid), dim3(kMxThreads), 0, s, pr, pc);
+    else hipLaunchKernelGGL((k_quant_dual_mx<kEden>), dim3(grid), dim3(kMxThreads), 0, s, pr, pc);
+  } else if (in_bf16) {
     if (fused) hipLaunchKernelGGL((k_quant_dual<1, kEdenFused>), dim3(grid), dim3(kThreads), 0, s, pr, pc);
     else hipLaunchKernelGGL((k_quant_dual<1, kEden>), dim3(grid), dim3(kThreads), 0, s, pr, pc);
   } else {
