@@ -720,6 +720,42 @@ __device__ __forceinline__ void mx_store(const QuadOut &q, uint32_t gb0, bool ac
   }
 }
 
+// The column kernel's stores: a column's two groups of a tile (128 bytes of
+// codes) are held by lanes (g, h) = (j / 16, h) of that column, 32 bytes
+// each.  Lanes j and j ^ 16 trade the 16-byte halves that belong to the
+// other store, so that each of the two code stores writes one whole group:
+// 64 contiguous bytes per column from four lanes, instead of four separate
+// 16-byte pieces.  Targets and scales are already contiguous per column.
+template <int MODE>
+__device__ __forceinline__ void mx_store_cols(const QuadOut &q, uint32_t gb0, uint32_t g, uint32_t h, bool col_ok,
+                                              bool grp1_ok, const QuantParams &p) {
+  if constexpr (MODE != kAmax && MODE != kRot) {
+    uint32_t send[4], recv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      send[k] = g ? q.c[k] : q.c[4 + k];
+      recv[k] = (uint32_t)__shfl_xor((int)send[k], 16, kWave);
+    }
+    // this lane's group's codes start at byte 8 (gb0 - 4h); group 0's at 64 g
+    // bytes before that
+    uint8_t *const base0 = p.codes + (size_t)(gb0 - 4u * h) * 8 - 64u * g;
+    if (col_ok) {
+      const uint4 a = g ? make_uint4(recv[0], recv[1], recv[2], recv[3]) : make_uint4(q.c[0], q.c[1], q.c[2], q.c[3]);
+      *reinterpret_cast<uint4 *>(base0 + 32u * h + 16u * g) = a;
+    }
+    if (col_ok && grp1_ok) {
+      const uint4 b = g ? make_uint4(q.c[4], q.c[5], q.c[6], q.c[7]) : make_uint4(recv[0], recv[1], recv[2], recv[3]);
+      *reinterpret_cast<uint4 *>(base0 + 64u + 32u * h + 16u * g) = b;
+    }
+    if (col_ok && (g == 0u || grp1_ok)) {
+      if constexpr (MODE == kEden || MODE == kIf4Eden)
+        *reinterpret_cast<float4 *>(p.tb + gb0) = make_float4(q.t[0], q.t[1], q.t[2], q.t[3]);
+      else
+        *reinterpret_cast<uint32_t *>(p.scales + gb0) = q.s;
+    }
+  }
+}
+
 // Axis 0, bf16 input, rotation on.  A wave tile is 32 consecutive groups of
 // the row-major group order (4096 elements; contiguous in memory for a dense
 // tensor); lane (j, h) rotates group j of the tile and codes its blocks
@@ -906,7 +942,7 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_cols_mx(QuantParams p) {
   float lmax = 0.0f, araw = 0.0f;
   QuadOut q;
   uint32_t gbq = 0u;
-  bool actq = false;
+  bool colq = false, grp1q = false;
   uint32_t T = first + (blockIdx.x >> 3);
   if (T < last) load_tile(T);
   for (; T < last; T += step) {
@@ -937,15 +973,16 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_cols_mx(QuantParams p) {
       // (columns past the last hold other data: masked)
       if (act) araw = fmaxf(araw, raw_absmax<1>(wd));
     }
-    mx_store<MODE>(q, gbq, actq, p);  // the previous tile's outputs
+    mx_store_cols<MODE>(q, gbq, j >> 4, h, colq, grp1q, p);  // the previous tile's outputs
     if (T + step < last) load_tile(T + step);
     f32x16_t acc[4];
     mx_rotate(fr, xb, lane, acc);
     gbq = col * p.K16 + 8u * grp + 4u * h;
-    actq = act;
-    mx_code4<MODE>(acc, gbq, actq, p, s_t, lmax, q);
+    colq = col < p.cols;
+    grp1q = 2u * tp + 1u < ngroups;
+    mx_code4<MODE>(acc, gbq, act, p, s_t, lmax, q);
   }
-  mx_store<MODE>(q, gbq, actq, p);
+  mx_store_cols<MODE>(q, gbq, j >> 4, h, colq, grp1q, p);
   if constexpr (writes_partials(MODE)) {
     const float m = block_max(lmax, red, kMxThreads);
     if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
