@@ -659,6 +659,88 @@ struct SlotSink {
   __device__ __forceinline__ void target(float v) const { q.t[n] = v; }
 };
 
+// MS-EDEN (FP4 codes, no INT branch) of a lane's four blocks with the
+// correction's sums as fused multiply-adds: N = sum z^2 and, per block,
+// sum z g (g the signed E2M1 values), so that D = sum z zhat is
+// sum_blocks s_b (sum z g) -- one instruction per element for each sum
+// instead of a product, a second product and a tree of additions.  The
+// codes and the block scales s_b are those of the exact rule (eden_codes);
+// the sums and the quotient N / D differ from its pairwise trees only in
+// rounding.  A block maximum below 2^-50 (other than zero) anywhere in the
+// wave, or a sum that is not finite, leaves the wave to the exact rule: the
+// function then returns false and has written nothing.  gb0 is a multiple
+// of 4, so that the four blocks share one Philox call of the fused variant.
+template <int MODE>
+__device__ __forceinline__ bool mx_eden_fast(const f32x16_t (&acc)[4], uint32_t gb0, bool active,
+                                             const QuantParams &p, float s_t, float &lmax, QuadOut &q) {
+  float sb[4], nb[4], db[4];
+  uint32_t lo[4], hi[4];
+  bool ok = true;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    float z[16], a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      z[r] = acc[n][r] * kRotNorm;
+      a = fmaxf(a, fabsf(z[r]));
+    }
+    ok = ok && !(a > 0.0f && a < 0x1p-50f);
+    sb[n] = div_by<6>(a);
+    const float rs = (a > 0.0f) ? rcp_rn(sb[n]) : 0.0f;  // 0: signed zero codes
+    float y[16], g[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[r] = z[r] * rs;
+    e2m1x16_rne(y, lo[n], hi[n]);
+    e2m1x16_value(lo[n], hi[n], g);
+    float s0 = 0.0f, s1 = 0.0f, d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      s0 = __builtin_fmaf(z[r], z[r], s0);
+      s1 = __builtin_fmaf(z[r + 1], z[r + 1], s1);
+      d0 = __builtin_fmaf(z[r], g[r], d0);
+      d1 = __builtin_fmaf(z[r + 1], g[r + 1], d1);
+    }
+    nb[n] = s0 + s1;
+    db[n] = sb[n] * (d0 + d1);
+  }
+  float c[4];  // t_b = s_b * c
+  if (p.group16) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      ok = ok && nb[n] <= 0x1.fffffep127f && db[n] <= 0x1.fffffep127f;
+      c[n] = (db[n] > 0.0f) ? nb[n] * __builtin_amdgcn_rcpf(db[n]) : 1.0f;
+    }
+  } else {
+    float N = (nb[0] + nb[1]) + (nb[2] + nb[3]);
+    float D = (db[0] + db[1]) + (db[2] + db[3]);
+    const auto pn = __builtin_amdgcn_permlane32_swap(__float_as_uint(N), __float_as_uint(N), false, false);
+    const auto pd = __builtin_amdgcn_permlane32_swap(__float_as_uint(D), __float_as_uint(D), false, false);
+    N = __uint_as_float(pn[0]) + __uint_as_float(pn[1]);
+    D = __uint_as_float(pd[0]) + __uint_as_float(pd[1]);
+    ok = ok && N <= 0x1.fffffep127f && D <= 0x1.fffffep127f;
+    const float cg = (D > 0.0f) ? N * __builtin_amdgcn_rcpf(D) : 1.0f;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) c[n] = cg;
+  }
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) return false;
+  Philox4 u;
+  if constexpr (MODE == kEdenFused) u = uniforms8(p.key, (uint64_t)(gb0 >> 3), 1u);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const float t = sb[n] * c[n];
+    q.c[2 * n] = lo[n];
+    q.c[2 * n + 1] = hi[n];
+    if constexpr (MODE == kEden) {
+      q.t[n] = t;
+      if (active) lmax = fmaxf(lmax, t);
+    } else {
+      const uint32_t e = e4m3_sr_sat(fminf(div_rn(t, s_t), 448.0f), uniform_at(u, (int)((gb0 & 7u) + n)));
+      q.s |= e << (8 * n);
+    }
+  }
+  return true;
+}
+
 // Code the lane's four blocks (accumulators acc, first block gb0) into q
 // (mx_store writes them).  MS-EDEN's group of 128 is the two lane halves' 4 + 4 blocks: the
 // sums add in the same pairwise tree as the 8-lane groups of the butterfly
@@ -668,6 +750,9 @@ __device__ __forceinline__ void mx_code4(f32x16_t (&acc)[4], uint32_t gb0, bool 
                                          float s_t, float &lmax, QuadOut &q) {
   constexpr bool EDEN = MODE == kEden || MODE == kEdenFused || MODE == kIf4Eden || MODE == kIf4EdenFused;
   q.s = 0u;
+  if constexpr (MODE == kEden || MODE == kEdenFused) {
+    if (mx_eden_fast<MODE>(acc, gb0, active, p, s_t, lmax, q)) return;
+  }
   if constexpr (EDEN) {
     EdenBlock b[4];
 #pragma unroll
