@@ -160,7 +160,7 @@ __device__ __forceinline__ uint32_t e4m3_ceil_sat(float v) {
 // (Written without early returns, so that the compiler selects instead of
 // branching per value; for a >= 448 or a <= 0 the rounding's intermediates
 // are discarded.)
-__device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
+__device__ __forceinline__ uint32_t e4m3_sr_sat_float(float a, uint32_t u16) {
   const int E = ilog2_floor_clamped(a, -6);
   const float y = a * pow2i(3 - E);
   const float f = floorf(y);
@@ -168,6 +168,25 @@ __device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
   const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
   const uint32_t e = (uint32_t)((E + 6) * 8 + (int)f) + up;
   return (a >= 448.0f) ? 0x7Eu : ((a > 0.0f) ? e : 0u);
+}
+
+// The same rounding with one integer addition in the normal range
+// [2^-6, 448].  There the gap is one unit of the fp32 mantissa's third bit,
+// and frac * 2^20 is m, the 20 mantissa bits below it: u16 < m / 16 holds
+// iff m >= 16 u16 + 1, iff adding 2^20 - 1 - 16 u16 to the bit pattern
+// carries into bit 20.  Bits 30..20 of the sum are then (E + 127) * 8 + q
+// plus the carry (which rolls q = 8 into the next binade, as the E4M3 grid
+// does), 960 above the E4M3 byte (E + 6) * 8 + q; 448 itself (E = 8, q = 6,
+// m = 0) gives 0x7E.  Other values (subnormal scales, zero, above 448) take
+// the float form, in the lanes that hold one.
+__device__ __forceinline__ uint32_t e4m3_sr_sat(float a, uint32_t u16) {
+  const uint32_t b = __float_as_uint(a);
+  uint32_t e = (b + ((u16 << 4) ^ 0xFFFFFu) - (960u << 20)) >> 20;  // 2^20 - 1 - 16 u16
+  const bool other = !(a >= 0x1p-6f && a <= 448.0f);
+  if (__builtin_amdgcn_ballot_w64(other) != 0) {
+    if (other) e = e4m3_sr_sat_float(a, u16);
+  }
+  return e;
 }
 
 // ---------------------------------------------------------------- E2M1

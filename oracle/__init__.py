@@ -55,6 +55,8 @@ def lib():
     L.orc_e2m1_rne_run.argtypes = [_U32, _U64, _P]
     L.orc_e4m3_run.restype = None
     L.orc_e4m3_run.argtypes = [_U32, _U64, _INT, _P]
+    L.orc_sr_e4m3_pairs.restype = None
+    L.orc_sr_e4m3_pairs.argtypes = [_P, _P, _U64, _P]
     L.orc_philox4x32_10.restype = None
     L.orc_philox4x32_10.argtypes = [_P, _P, _P]
     L.orc_uniform16.restype = _U32
@@ -151,6 +153,16 @@ def e4m3_run(bits_lo, count, ceil_mode=False):
     bits_lo .. bits_lo+count-1."""
     out = np.empty(count, dtype=np.uint8)
     lib().orc_e4m3_run(int(bits_lo), int(count), int(bool(ceil_mode)), _ptr(out))
+    return out
+
+
+def sr_e4m3_pairs(a, u16):
+    """E4M3 bytes of the stochastic scale rounding, orc_sr_e4m3(a[i], u16[i])."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u16 = np.ascontiguousarray(u16, dtype=np.uint16)
+    assert a.shape == u16.shape
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib().orc_sr_e4m3_pairs(_ptr(a), _ptr(u16), int(a.size), _ptr(out))
     return out
 
 

@@ -225,6 +225,14 @@ void orc_e4m3_run(uint32_t bits_lo, uint64_t count, int ceil_mode, uint8_t *byte
   }
 }
 
+/* The scale rounding of MS-EDEN's second half over given pairs:
+ * bytes[i] = orc_sr_e4m3(a[i], u16[i]) (exhaustive and boundary checks of
+ * the device's form; no arithmetic beyond the function it loops). */
+void orc_sr_e4m3_pairs(const float *a, const uint16_t *u16, uint64_t n, uint8_t *bytes) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)n; i++) bytes[i] = (uint8_t)orc_sr_e4m3(a[i], u16[i]);
+}
+
 /* ======================================================================
  * Counter-based RNG: Philox-4x32 with 10 rounds [Philox].
  * Each round multiplies words 0 and 2 by the two round multipliers, swaps

@@ -44,6 +44,7 @@ float orc_sr_expected_sq(float a, int is_int); /* (a-l)(u-a) on E2M1 / 0..7 */
 /* the rules above over consecutive fp32 bit patterns (exhaustive checks) */
 void orc_e2m1_rne_run(uint32_t bits_lo, uint64_t count, uint8_t *codes);
 void orc_e4m3_run(uint32_t bits_lo, uint64_t count, int ceil_mode, uint8_t *bytes);
+void orc_sr_e4m3_pairs(const float *a, const uint16_t *u16, uint64_t n, uint8_t *bytes);
 
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 uint32_t orc_uniform16(uint64_t seed, uint32_t tag, uint32_t stream, uint64_t idx);

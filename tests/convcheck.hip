@@ -6,6 +6,8 @@
 //   - e2m1x16_rne: gfx950's packed fp32 -> E2M1 conversion (round to nearest
 //     even, saturating, sign kept), over any run of fp32 bit patterns;
 //   - e4m3_rne_sat / e4m3_ceil_sat: the block-scale roundings, over any run;
+//   - e4m3_sr_sat: MS-EDEN's stochastic scale rounding, over given pairs
+//     (value, 16-bit uniform);
 //   - div_by<6> / div_by<7>: the block maximum divided by 6 and 7, against
 //     the device's IEEE division, over every finite a >= 0;
 //   - e2m1x16_value, e4m3x2_f16, e4m3_value, dequant8 and dequant8_lut: the
@@ -36,6 +38,12 @@ __global__ void k_e4m3(uint32_t bits_lo, uint32_t count, int ceil_mode, uint8_t 
   if (i >= count) return;
   const float v = __uint_as_float(bits_lo + i);
   out[i] = (uint8_t)(ceil_mode ? nv4::e4m3_ceil_sat(v) : nv4::e4m3_rne_sat(v));
+}
+
+__global__ void k_e4m3_sr(const float *a, const uint16_t *u, uint32_t count, uint8_t *out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  out[i] = (uint8_t)nv4::e4m3_sr_sat(a[i], u[i]);
 }
 
 struct Mismatch {
@@ -148,6 +156,23 @@ int convcheck_e4m3(uint32_t bits_lo, uint32_t count, int ceil_mode, uint8_t *hos
   if (e != hipSuccess) return (int)e;
   hipLaunchKernelGGL(k_e4m3, dim3((count + 255) / 256), dim3(256), 0, 0, bits_lo, count, ceil_mode, d);
   const int st = to_host(host_bytes, d, count);
+  hipFree(d);
+  return st;
+}
+
+// E4M3 bytes of the stochastic rounding of host pairs (a[i], u[i]).
+int convcheck_e4m3_sr(const float *a, const uint16_t *u, uint32_t count, uint8_t *host_bytes) {
+  char *d = nullptr;
+  const size_t n = count ? count : 1;
+  hipError_t e = hipMalloc(&d, n * 7);
+  if (e != hipSuccess) return (int)e;
+  float *da = reinterpret_cast<float *>(d);
+  uint16_t *du = reinterpret_cast<uint16_t *>(d + n * 4);
+  uint8_t *dout = reinterpret_cast<uint8_t *>(d + n * 6);
+  e = hipMemcpy(da, a, (size_t)count * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(du, u, (size_t)count * 2, hipMemcpyHostToDevice);
+  if (e == hipSuccess) hipLaunchKernelGGL(k_e4m3_sr, dim3((count + 255) / 256), dim3(256), 0, 0, da, du, count, dout);
+  const int st = e == hipSuccess ? to_host(host_bytes, dout, count) : (int)e;
   hipFree(d);
   return st;
 }

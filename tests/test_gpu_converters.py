@@ -14,6 +14,11 @@ includes the kernels' header) over its whole input domain:
   E2M1 range [0, 6], the saturation range above it, the infinities), against
   the nibble sign<<3 | E2M1_RNE(min(|y|, 6)) of the oracle's block coding;
 - e4m3_rne_sat and e4m3_ceil_sat on every finite v >= 0 and +inf;
+- e4m3_sr_sat (MS-EDEN's stochastic scale rounding, an integer addition on
+  the bit pattern in the normal range) on every fp32 value in [0, 448] with
+  a uniform per value, and at every decision boundary: for each of the
+  65536 uniforms, the values whose position in the gap sits exactly on the
+  threshold and one unit either side, in every binade and every gap;
 - div_by<6>, div_by<7> on every finite a >= 0, against the IEEE quotient;
 - every code byte through both E2M1 decoders and both IF4 tables, every
   scale byte through the E4M3 decoders, and every (scale byte, code byte)
@@ -43,6 +48,7 @@ def cc():
     u32, P = ctypes.c_uint32, ctypes.c_void_p
     lib.convcheck_e2m1_rne.argtypes = [u32, u32, P]
     lib.convcheck_e4m3.argtypes = [u32, u32, ctypes.c_int, P]
+    lib.convcheck_e4m3_sr.argtypes = [P, P, u32, P]
     lib.convcheck_div_by.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(u32)]
     lib.convcheck_decoders.argtypes = [P] * 7
     return lib
@@ -92,6 +98,60 @@ def test_e4m3_block_scale_every_value(cc, orc, ceil_mode):
         want = orc.e4m3_run(lo, n, ceil_mode)
         assert np.array_equal(got, want), _first_diff(got, want, lo, 1)
     print(f"e4m3 {'ceil' if ceil_mode else 'rne'}: {time.time() - t0:.1f} s", flush=True)
+
+
+def _uniforms_of(bits):
+    """A 16-bit uniform per value: the high half of a multiplicative hash of
+    its bit pattern, so that neighbouring values meet unrelated uniforms."""
+    return ((bits.astype(np.uint32) * np.uint32(0x9E3779B1)) >> np.uint32(16)).astype(np.uint16)
+
+
+def _sr_compare(cc, orc, a, u, what):
+    got = np.empty(a.size, dtype=np.uint8)
+    assert cc.convcheck_e4m3_sr(_ptr(a), _ptr(u), a.size, _ptr(got)) == 0
+    want = orc.sr_e4m3_pairs(a, u)
+    if not np.array_equal(got, want):
+        i = int(np.flatnonzero(got != want)[0])
+        raise AssertionError(f"{what}: a bits {a.view(np.uint32)[i]:#010x}, u16 {u[i]}: device {got[i]:#04x}, "
+                             f"oracle {want[i]:#04x}")
+
+
+def test_e4m3_sr_every_value(cc, orc):
+    """Every fp32 value in [0, 448] (the range the MS-EDEN scale reaches after
+    its clamp), then -0, +inf, NaN and values above 448."""
+    end = 0x43E00000 + 1           # 448 = 0x43E00000
+    t0 = time.time()
+    for lo in range(0, end, CHUNK):
+        bits = np.arange(lo, min(lo + CHUNK, end), dtype=np.uint32)
+        _sr_compare(cc, orc, bits.view(np.float32), _uniforms_of(bits), "e4m3 SR")
+    odd = np.array([0x80000000, 0x7F800000, 0x7FC00000, 0x43E00001, 0x43E0FFFF, 0x44000000, 0x7F7FFFFF], np.uint32)
+    for u in (0, 1, 0x8000, 0xFFFF):
+        _sr_compare(cc, orc, odd.view(np.float32), np.full(odd.size, u, np.uint16), "e4m3 SR outside [0, 448]")
+    print(f"e4m3 SR: {time.time() - t0:.1f} s", flush=True)
+
+
+def test_e4m3_sr_decision_boundaries(cc, orc):
+    """The decision u16 < frac * 65536 at its threshold, for every uniform:
+    normal values with the 20 mantissa bits below the kept three equal to
+    16 u16 - 1, 16 u16, 16 u16 + 1 (binades 2^-6 .. 2^8, every gap), and
+    E4M3-subnormal values (f + u16 / 65536) * 2^-9 and their fp32
+    neighbours."""
+    u = np.arange(65536, dtype=np.int64)
+    A, U = [], []
+    for E in range(-6, 9):
+        for q in range(8):
+            for d in (-1, 0, 1):
+                m = np.clip(16 * u + d, 0, (1 << 20) - 1)
+                A.append((((E + 127) << 23) | (q << 20) | m).astype(np.uint32))
+                U.append(u)
+    for f in range(8):
+        b = ((f + u / 65536.0) * 2.0 ** -9).astype(np.float32).view(np.uint32)
+        for d in (-1, 0, 1):
+            A.append((b.astype(np.int64) + d).clip(0).astype(np.uint32))
+            U.append(u)
+    bits, uu = np.concatenate(A), np.concatenate(U).astype(np.uint16)
+    keep = bits <= 0x43E00000
+    _sr_compare(cc, orc, bits[keep].view(np.float32), uu[keep], "e4m3 SR boundary")
 
 
 @pytest.mark.parametrize("d", [6, 7])

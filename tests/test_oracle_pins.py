@@ -509,6 +509,18 @@ def test_msededen_scale_expectation_is_target(orc):
         assert abs(vals.mean() - np.float64(a)) <= gap * 2.0 ** -16 + 1e-12
 
 
+def test_sr_e4m3_pairs_is_the_scalar_rule(orc):
+    """The array form used by the device's exhaustive check loops the scalar
+    rule: same bytes on values across the grid, at grid points, at the top,
+    and on zero."""
+    rng = np.random.default_rng(31)
+    a = np.concatenate([rng.uniform(0, 448, 3000), 2.0 ** rng.uniform(-12, 8.8, 3000),
+                        [0.0, 448.0, 2.0 ** -6, 2.0 ** -9, 416.0, 1.0]]).astype(np.float32)
+    u = rng.integers(0, 65536, a.size).astype(np.uint16)
+    want = np.array([orc.sr_e4m3(float(x), int(v)) for x, v in zip(a, u)], dtype=np.uint8)
+    assert np.array_equal(orc.sr_e4m3_pairs(a, u), want)
+
+
 # ------------------------------------------------------------------ GEMM
 def test_gemm_against_numpy_matmul(orc):
     rng = np.random.default_rng(16)
