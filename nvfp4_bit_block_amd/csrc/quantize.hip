@@ -1300,9 +1300,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
 // (lane (j, h): two transposing reads per step, as in k_quant_cols_mx), with
 // the same fragments.  f spreads the 4 rows of a transposing read over 4
 // different 64-byte bank groups, and the 32 rows of a row read over 16
-// chunk positions (two rows per bank group).  The row pass is coded first;
-// the next tile's loads are issued once the column operands are read too.  Tiles run with the
-// column block fastest, each XCD taking a contiguous share, so that a row's
+// chunk positions (two rows per bank group).  The row operands go through
+// their MFMAs and the column operands are read before either axis is coded:
+// the next tile's loads are issued then, and overlap all of the coding
+// (the row accumulators and the column operands stay live across it: about
+// 180 VGPRs, two waves per SIMD).  Tiles run with the column block fastest, each XCD taking a contiguous share, so that a row's
 // successive 64-byte code runs are written by one L2.  pr / pc: the
 // row-wise (axis 0) and column-wise (axis 1) outputs.
 template <int MODE>
@@ -1364,12 +1366,20 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
   float lmax_r = 0.0f, lmax_c = 0.0f;
   uint32_t T = first + (blockIdx.x >> 3);
   if (T < last) load_tile(T);
-  for (; T < last; T += step) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the tile
-    __builtin_amdgcn_s_barrier();        // ... and every wave's
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the first tile
+  for (bool later = false; T < last; T += step, later = true) {
+    // This wave's part of the tile.  A later tile's loads were issued before
+    // the previous tile's six output stores (two 16-byte code stores and
+    // one 16-byte store of targets or scales per axis, each a single
+    // instruction), so waiting for all but the last six memory operations
+    // waits for the loads and leaves those stores in flight.
+    if (later) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+    __builtin_amdgcn_s_barrier();                   // ... and every wave's
     const uint32_t rb = fdiv(8u * T, pr.k16div), cb = T - rb * ncb;
-    // rows first (operands, MFMAs, coding), then the column operands; the
-    // next tile's loads go out once both have been read
+    // the row operands and their MFMAs, then the column operands; the next
+    // tile's loads go out once both have been read, before either axis is
+    // coded, so that the loads overlap all of the coding
+    f32x16_t acc[4];
     {
       uint4 xr[8];
 #pragma unroll
@@ -1378,14 +1388,8 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
         const uint2 b = *reinterpret_cast<const uint2 *>(st8 + 256u * rr + 16u * ((2u * t + 1u) ^ fr_r) + 8u * h);
         xr[t] = make_uint4(a.x, a.y, b.x, b.y);
       }
-      f32x16_t acc[4];
       mx_rotate(fr, xr, lane, acc);
-      QuadOut q;
-      const uint32_t gb0 = (128u * rb + rr) * pr.K16 + 8u * cb + 4u * h;
-      mx_code4<MODE>(acc, gb0, true, pr, s_r, lmax_r, q);
-      mx_store<MODE>(q, gb0, true, pr);
     }
-    __builtin_amdgcn_sched_barrier(0);
     uint4 xc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -1403,7 +1407,12 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
     __builtin_amdgcn_s_barrier();        // every wave's: the stage is free
     if (T + step < last) load_tile(T + step);
     {
-      f32x16_t acc[4];
+      QuadOut q;
+      const uint32_t gb0 = (128u * rb + rr) * pr.K16 + 8u * cb + 4u * h;
+      mx_code4<MODE>(acc, gb0, true, pr, s_r, lmax_r, q);
+      mx_store<MODE>(q, gb0, true, pr);
+    }
+    {
       mx_rotate(fr, xc, lane, acc);
       QuadOut q;
       const uint32_t gb0 = (128u * cb + 32u * w + j) * pc.K16 + 8u * rb + 4u * h;
