@@ -463,6 +463,31 @@ def test_matrix_core_rotation_layouts(nv, axis):
                                      what=f"{name} rotation axis{axis}")
 
 
+@pytest.mark.parametrize("group", [128, 16])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_matrix_core_mseden_small_blocks(nv, axis, group):
+    """MS-EDEN on the matrix cores with 128-groups scaled to about 1e-18 (block
+    maxima below 2^-50, where the kernels leave the wave to the exact rule
+    instead of the fused sums) and all-zero groups, among Gaussian ones: the
+    waves that hold them and those that do not both match the oracle under
+    the rotation rule."""
+    rng = np.random.default_rng(53)
+    signs = synth.signs_from_rng(rng)
+    x = synth.gaussian(256, 512, seed=54)
+    if axis == 0:
+        x[5:9, 128:256] *= np.float32(1e-18)       # groups of rows 5..8
+        x[40, 256:384] = 0.0
+        x[200:202, :] *= np.float32(3e-19)
+    else:
+        x[128:256, 7:11] *= np.float32(1e-18)      # groups of columns 7..10
+        x[0:128, 300] = 0.0
+        x[:, 450:452] *= np.float32(3e-19)
+    x = synth.to_bf16_f32(x)
+    g = _run(nv, x, "bf16", "mseden", axis, signs, group=group)
+    r = _ref(x, oracle.MSEDEN, axis, signs, group=group)
+    assert_rotated_close(g, r, what=f"small blocks axis{axis} group{group}")
+
+
 def test_strided_input(nv):
     """A row-major view with leading dimension above the row length."""
     import torch
