@@ -1300,13 +1300,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantParams pr, QuantPa
 // (lane (j, h): two transposing reads per step, as in k_quant_cols_mx), with
 // the same fragments.  f spreads the 4 rows of a transposing read over 4
 // different 64-byte bank groups, and the 32 rows of a row read over 16
-// chunk positions (two rows per bank group).  The row operands go through
-// their MFMAs and the column operands are read before either axis is coded:
-// the next tile's loads are issued then, and overlap all of the coding
-// (the row accumulators and the column operands stay live across it: about
-// 180 VGPRs, two waves per SIMD).  Tiles run with the column block fastest, each XCD taking a contiguous share, so that a row's
-// successive 64-byte code runs are written by one L2.  pr / pc: the
-// row-wise (axis 0) and column-wise (axis 1) outputs.
+// chunk positions (two rows per bank group).  Two stages (80 KB of LDS with
+// the fragments, two workgroups per CU, all resident): tile T is read from
+// one while tile T + step loads into the other, issued as soon as every
+// wave is done with the previous tile, so each load has a whole tile's work
+// to land.  Tiles run with the column block fastest, each XCD taking a
+// contiguous share, so that a row's successive 64-byte code runs are
+// written by one L2.  pr / pc: the row-wise (axis 0) and column-wise
+// (axis 1) outputs.
 template <int MODE>
 __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, QuantParams pc) {
   typedef __attribute__((address_space(3))) void lds_void;
@@ -1314,8 +1315,12 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
   typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
   static_assert(kMxThreads == 256, "four waves of 32 rows and 32 columns");
   __shared__ RotFrags fr;
-  __shared__ uint4 stage[2048];  // 128 rows x 16 chunks
-  float *const red = reinterpret_cast<float *>(&stage[0]);
+  // two tiles of 128 rows x 16 chunks, as two objects: the compiler then
+  // sees that the loads into one do not touch the operand reads of the
+  // other (into one array with a variable index, it waits for the loads
+  // before every LDS read)
+  __shared__ uint4 stage0[2048], stage1[2048];
+  float *const red = reinterpret_cast<float *>(&stage0[0]);
   float s_r = 1.0f, s_c = 1.0f;
   if constexpr (MODE == kEdenFused) {
     s_r = *pr.ts_in;
@@ -1344,7 +1349,7 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
     const uint32_t r = 32u * w + 4u * i + (lane >> 4);
     voff[i] = r * row_bytes + 16u * ((lane & 15u) ^ swz(r));
   }
-  auto load_tile = [&](uint32_t T) {
+  auto load_tile = [&](uint32_t T, uint4 *dst) {
     const uint32_t rb = fdiv(8u * T, pr.k16div), cb = T - rb * ncb;
     const uint64_t base = (uint64_t)rb * 128u * row_bytes + 256u * cb;
     const uint64_t left = end > base ? end - base : 0;
@@ -1353,9 +1358,8 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
         (int)(left < 0x7FFFFFFFull ? left : 0x7FFFFFFFull), kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&stage[64u * (8u * w + i)], 16, voff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&dst[64u * (8u * w + i)], 16, voff[i], 0, 0, 0);
   };
-  const uint8_t *const st8 = reinterpret_cast<const uint8_t *>(&stage[0]);
   // row reads: row rr = 32w + j, chunk (2t + e2) ^ f(rr), byte 8h
   const uint32_t rr = 32u * w + j, fr_r = swz(rr);
   // transposing reads: lane (G = l / 16, s = l % 16) points at row
@@ -1364,21 +1368,21 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
   const uint32_t sl = lane & 15u, g16 = lane >> 4;
   const uint32_t ccol = 32u * w + 16u * (g16 & 1u) + 4u * (sl & 3u);
   float lmax_r = 0.0f, lmax_c = 0.0f;
-  uint32_t T = first + (blockIdx.x >> 3);
-  if (T < last) load_tile(T);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the first tile
-  for (bool later = false; T < last; T += step, later = true) {
-    // This wave's part of the tile.  A later tile's loads were issued before
+  // One tile: T's operands from stage cur while the next tile's loads go to
+  // stage nxt.
+  auto tile = [&](uint32_t T, bool later, const uint4 *cur, uint4 *nxt) {
+    // This wave's part of tile T.  A later tile's loads were issued before
     // the previous tile's six output stores (two 16-byte code stores and
     // one 16-byte store of targets or scales per axis, each a single
     // instruction), so waiting for all but the last six memory operations
     // waits for the loads and leaves those stores in flight.
     if (later) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
-    __builtin_amdgcn_s_barrier();                   // ... and every wave's
+    // every wave's part of tile T has landed, and every wave is done with
+    // the other stage (the previous tile's operands are in registers)
+    __builtin_amdgcn_s_barrier();
+    if (T + step < last) load_tile(T + step, nxt);
+    const uint8_t *const st8 = reinterpret_cast<const uint8_t *>(cur);
     const uint32_t rb = fdiv(8u * T, pr.k16div), cb = T - rb * ncb;
-    // the row operands and their MFMAs, then the column operands; the next
-    // tile's loads go out once both have been read, before either axis is
-    // coded, so that the loads overlap all of the coding
     f32x16_t acc[4];
     {
       uint4 xr[8];
@@ -1390,22 +1394,6 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
       }
       mx_rotate(fr, xr, lane, acc);
     }
-    uint4 xc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint2 v[2];
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const uint32_t r = 16u * t + 8u * e2 + 4u * (g16 >> 1) + (sl >> 2);
-        const s16x4_t x4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(st8 + 256u * r + 16u * ((ccol >> 3) ^ swz(r)) + 2u * (ccol & 7u)));
-        v[e2] = __builtin_bit_cast(uint2, x4);
-      }
-      xc[t] = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the operands are in registers
-    __builtin_amdgcn_s_barrier();        // every wave's: the stage is free
-    if (T + step < last) load_tile(T + step);
     {
       QuadOut q;
       const uint32_t gb0 = (128u * rb + rr) * pr.K16 + 8u * cb + 4u * h;
@@ -1413,12 +1401,36 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_dual_mx(QuantParams pr, Qu
       mx_store<MODE>(q, gb0, true, pr);
     }
     {
+      uint4 xc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        uint2 v[2];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const uint32_t r = 16u * t + 8u * e2 + 4u * (g16 >> 1) + (sl >> 2);
+          const s16x4_t x4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(st8 + 256u * r + 16u * ((ccol >> 3) ^ swz(r)) + 2u * (ccol & 7u)));
+          v[e2] = __builtin_bit_cast(uint2, x4);
+        }
+        xc[t] = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
+      }
       mx_rotate(fr, xc, lane, acc);
       QuadOut q;
       const uint32_t gb0 = (128u * cb + 32u * w + j) * pc.K16 + 8u * rb + 4u * h;
       mx_code4<MODE>(acc, gb0, true, pc, s_c, lmax_c, q);
       mx_store<MODE>(q, gb0, true, pc);
     }
+  };
+  uint32_t T = first + (blockIdx.x >> 3);
+  if (T < last) load_tile(T, stage0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the first tile
+  // tiles alternate between the stages: the loop body is written out twice
+  for (bool later = false; T < last; later = true) {
+    tile(T, later, stage0, stage1);
+    T += step;
+    if (T >= last) break;
+    tile(T, true, stage1, stage0);
+    T += step;
   }
   if constexpr (MODE == kEden) {
     const float mr = block_max(lmax_r, red, kMxThreads);
@@ -1568,8 +1580,16 @@ static bool use_dual_mx(const QuantParams &pr, int in_bf16) {
 
 uint32_t dual_grid(const QuantParams &pr, int in_bf16) {
   if (use_dual_mx(pr, in_bf16)) {
+    // two workgroups per compute unit (80 KB of LDS each), all resident:
+    // each loops over its XCD's tiles with its loads one tile ahead
     const uint64_t tiles = (uint64_t)(pr.rows / 128) * (pr.cols / 128);
-    const uint64_t g = (tiles + 7) / 8 * 8;
+    uint64_t g = (tiles + 7) / 8 * 8;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 8) {
+      const uint64_t resident = (uint64_t)(2 * cus / 8) * 8;
+      if (g > resident) g = resident;
+    }
     return (uint32_t)(g < (uint64_t)kMaxPartials ? g : kMaxPartials);
   }
   const uint32_t width = 4u * (in_bf16 ? ColCfg<1>::kTileCols : ColCfg<0>::kTileCols);
