@@ -196,7 +196,7 @@ int quantize_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, int64
       e = launch_quant(p, bf, o->axis, if4 ? kIf4Eden : kEden, grid, s);
       if (e == hipSuccess) {
         p.npartial = grid;
-        e = launch_eden_scales(p, eden_scales_grid(p), s);
+        e = launch_eden_scales(p, if4, eden_scales_grid(p), s);
       }
     }
   } else {
@@ -255,8 +255,8 @@ int quantize_dual_impl(const void *x, int in_dtype, int64_t rows, int64_t cols, 
   if (e == hipSuccess && !o->tensor_scale_in) {
     pr.npartial = grid;
     pc.npartial = grid;
-    e = launch_eden_scales(pr, eden_scales_grid(pr), s);
-    if (e == hipSuccess) e = launch_eden_scales(pc, eden_scales_grid(pc), s);
+    e = launch_eden_scales(pr, false, eden_scales_grid(pr), s);
+    if (e == hipSuccess) e = launch_eden_scales(pc, false, eden_scales_grid(pc), s);
   }
   if (e != hipSuccess) return fail(NVFP4_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();

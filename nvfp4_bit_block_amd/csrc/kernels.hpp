@@ -75,7 +75,8 @@ struct QuantParams {
 // in_bf16: 1 = bf16 input, 0 = fp32 input.
 hipError_t launch_quant(const QuantParams &p, int in_bf16, int axis, Mode mode, uint32_t grid,
                         hipStream_t s);
-hipError_t launch_eden_scales(const QuantParams &p, uint32_t grid, hipStream_t s);
+// if4: the targets' sign bits are IF4's INT flags.
+hipError_t launch_eden_scales(const QuantParams &p, bool if4, uint32_t grid, hipStream_t s);
 // Empty tensor: *ts = *ts_in (or 1), *amax_out = 0 if given.
 hipError_t launch_trivial_scale(float *ts, const float *ts_in, float *amax_out, hipStream_t s);
 // MS-EDEN along both axes from one read (fused = given tensor scales).

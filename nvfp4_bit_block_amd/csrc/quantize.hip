@@ -1447,8 +1447,30 @@ __device__ __forceinline__ uint32_t eden_scale_byte(float t, const Divisor &s_t,
   return e4m3_sr_sat(fminf(div_rn(fabsf(t), s_t), 448.0f), u16) | flag;
 }
 
+// The same byte where |t| and the quotient lie in their ordinary ranges --
+// the refined division's fast path exact (|t| in [2^-60, 2^60], s_t too)
+// and t / s_t in [2^-6, 448], where no clamp applies and the rounding is
+// the integer addition of e4m3_sr_sat -- with the general form for the
+// lanes outside them.  The same bytes as eden_scale_byte for every t; IF4:
+// the sign bit of t is the INT flag (NVFP4 targets are never negative).
+template <int IF4>
+__device__ __forceinline__ uint32_t eden_scale_byte_fix(float t, const Divisor &d, uint32_t u16) {
+  const float a = fabsf(t);
+  const float q0 = a * d.y;
+  const float r = __builtin_fmaf(-d.b, q0, a);
+  const float v = __builtin_fmaf(r, d.y, q0);
+  const bool fast = d.ok && a >= kDivLo && a <= kDivHi && v >= 0x1p-6f && v <= 448.0f;
+  uint32_t e = (__float_as_uint(v) + ((u16 << 4) ^ 0xFFFFFu) - (960u << 20)) >> 20;
+  if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
+    if (!fast) e = e4m3_sr_sat(fminf(div_rn(a, d), 448.0f), u16);
+  }
+  if constexpr (IF4) e |= (__float_as_uint(t) >> 24) & 0x80u;
+  return e;
+}
+
 // s_t = max t / 448 (or the given scale); scale = SR of min(t / s_t, 448)
 // onto the E4M3 grid, one Philox call per 8 consecutive blocks (tag 1).
+template <int IF4>
 __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
   __shared__ float red[kThreads / kWave];
   float s_t;
@@ -1474,7 +1496,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t e = eden_scale_byte(t[j], dst, uniform_at(u, j));
+      const uint32_t e = eden_scale_byte_fix<IF4>(t[j], dst, uniform_at(u, j));
       if (j < 4) lo |= e << (8 * j);
       else hi |= e << (8 * (j - 4));
     }
@@ -1625,8 +1647,9 @@ hipError_t launch_trivial_scale(float *ts, const float *ts_in, float *amax_out, 
   return hipGetLastError();
 }
 
-hipError_t launch_eden_scales(const QuantParams &p, uint32_t grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_eden_scales, dim3(grid), dim3(kThreads), 0, s, p);
+hipError_t launch_eden_scales(const QuantParams &p, bool if4, uint32_t grid, hipStream_t s) {
+  if (if4) hipLaunchKernelGGL(k_eden_scales<1>, dim3(grid), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(k_eden_scales<0>, dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
