@@ -590,7 +590,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kRotNorm = 0x1.6a09e6p-4f;  // fp32(1/sqrt(128)) = 0x3DB504F3
 
-__device__ __forceinline__ uint32_t mx_out0(uint32_t i) {
+__host__ __device__ constexpr uint32_t mx_out0(uint32_t i) {
   return ((i & 4u) << 4) | ((i >> 3) << 2) | (i & 3u);
 }
 
@@ -600,25 +600,75 @@ __device__ __forceinline__ uint32_t mx_out0(uint32_t i) {
 // bit 3 and the lane half -> bit 2, which puts the two lane halves' rows
 // four rows apart, on disjoint LDS banks.
 template <int AXIS>
-__device__ __forceinline__ uint32_t mx_in(uint32_t t, uint32_t h, uint32_t e) {
+__host__ __device__ constexpr uint32_t mx_in(uint32_t t, uint32_t h, uint32_t e) {
   if constexpr (AXIS == 0) return 16u * t + 8u * h + e;
   else return 16u * t + 8u * (e >> 2) + 4u * h + (e & 3u);
 }
 
 typedef uint4 RotFrags[16][64];
 
+// Byte v of kWalsh8: bit e is the parity of v & e (e, v = 0..7).
+constexpr uint64_t walsh8() {
+  uint64_t c = 0;
+  for (uint32_t v = 0; v < 8; ++v)
+    for (uint32_t e = 0; e < 8; ++e)
+      c |= (uint64_t)(__builtin_popcount(v & e) & 1) << (8 * v + e);
+  return c;
+}
+constexpr uint64_t kWalsh8 = walsh8();
+static_assert(kWalsh8 == 0x963C5AF066CCAA00ull, "Walsh patterns of 3-bit indices");
+
+// The decomposition mx_build_frags uses, checked at compile time for every
+// output row, step, lane half and slot: in(t, h, e) is the slot's base plus
+// its varying bits, popcount(o & k) splits accordingly, and the sign of
+// position k sits at bit sh + e (axis 0) or sh + 8 (e / 4) + e % 4 (axis 1)
+// of sign word t / 2.
+template <int AXIS>
+constexpr bool mx_frag_rule_holds() {
+  for (uint32_t i = 0; i < 32; ++i)
+    for (uint32_t t = 0; t < 8; ++t)
+      for (uint32_t h = 0; h < 2; ++h)
+        for (uint32_t e = 0; e < 8; ++e) {
+          const uint32_t o = mx_out0(i), k = mx_in<AXIS>(t, h, e), base = mx_in<AXIS>(t, h, 0);
+          const uint32_t v = AXIS == 0 ? (o & 7u) : ((o & 3u) | ((o >> 1) & 4u));
+          const uint32_t par = ((uint32_t)__builtin_popcount(o & base) + (uint32_t)(kWalsh8 >> (8 * v + e))) & 1u;
+          if (par != ((uint32_t)__builtin_popcount(o & k) & 1u)) return false;
+          const uint32_t sh = 16u * (t & 1u) + (AXIS == 0 ? 8u * h : 4u * h);
+          const uint32_t bit = AXIS == 0 ? sh + e : sh + 8u * (e >> 2) + (e & 3u);
+          if (32u * (t >> 1) + bit != k) return false;
+        }
+  return true;
+}
+static_assert(mx_frag_rule_holds<0>() && mx_frag_rule_holds<1>(), "fragment sign decomposition");
+
+// Fragment f = 2t + neg of lane l holds the bf16 signs
+// (-1)^(popcount(o & k) + s_k + neg), o = out(l % 32), k = in(t, l / 32, e),
+// e = 0..7.  The 8 positions of a slot are one base (the bits that do not
+// vary with e) plus 3 varying bits -- bits 0..2 of k on axis 0, bits 0, 1
+// and 3 on axis 1 -- so popcount(o & k) is popcount(o & base) plus the
+// parity of (o's varying bits) & e, one byte of kWalsh8; the random signs
+// s_k of the 8 positions are one byte (axis 0) or two nibbles (axis 1) of
+// the sign word.  Each wave builds whole fragments (f is wave-uniform), so
+// the sign word is read from scalar registers.
 template <int AXIS>
 __device__ __forceinline__ void mx_build_frags(const uint32_t sg[4], RotFrags &fr) {
-  for (uint32_t x = threadIdx.x; x < 16u * 64u; x += blockDim.x) {
-    const uint32_t f = x >> 6, l = x & 63u, t = f >> 1, neg = f & 1u;
-    const uint32_t o = mx_out0(l & 31u), h = l >> 5;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
+  const uint32_t l = threadIdx.x & 63u, h = l >> 5, o = mx_out0(l & 31u);
+  const uint32_t v = AXIS == 0 ? (o & 7u) : ((o & 3u) | ((o >> 1) & 4u));
+  const uint32_t walsh = (uint32_t)(kWalsh8 >> (8u * v)) & 0xFFu;
+  const uint32_t nw = blockDim.x >> 6;
+  for (uint32_t f = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); f < 16u; f += nw) {
+    const uint32_t t = f >> 1, neg = f & 1u;
+    const uint32_t word = (t >> 1) == 0u ? sg[0] : (t >> 1) == 1u ? sg[1] : (t >> 1) == 2u ? sg[2] : sg[3];
+    const uint32_t base = mx_in<AXIS>(t, h, 0u);
+    const uint32_t sh = 16u * (t & 1u) + (AXIS == 0 ? 8u * h : 4u * h);
+    const uint32_t sbits = AXIS == 0 ? ((word >> sh) & 0xFFu)
+                                     : (((word >> sh) & 0xFu) | (((word >> (sh + 8u)) & 0xFu) << 4));
+    const uint32_t flip = (((uint32_t)__builtin_popcount(o & base) + neg) & 1u) ? 0xFFu : 0u;
+    const uint32_t bits = walsh ^ sbits ^ flip;  // bit e set: slot e holds -1
+    uint32_t w[4];
 #pragma unroll
-    for (uint32_t e = 0; e < 8; ++e) {
-      const uint32_t k = mx_in<AXIS>(t, h, e);
-      const uint32_t sgn = ((uint32_t)__builtin_popcount(o & k) + ((sg[k >> 5] >> (k & 31u)) & 1u) + neg) & 1u;
-      w[e >> 1] |= (0x3F80u | (sgn << 15)) << (16u * (e & 1u));  // bf16 +-1
-    }
+    for (uint32_t i = 0; i < 4; ++i)  // bf16 +-1 pairs: slots 2i (low half) and 2i + 1
+      w[i] = 0x3F803F80u | ((bits << (15u - 2u * i)) & 0x8000u) | ((bits << (30u - 2u * i)) & 0x80000000u);
     fr[f][l] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -862,13 +912,6 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_rows_mx(QuantParams p) {
   __shared__ uint4 stage[kMxThreads / kWave][512];
   // (the reductions before and after the loop use the stage's first bytes)
   float *const red = reinterpret_cast<float *>(&stage[0][0]);
-  float s_t = 1.0f;
-  if constexpr (takes_tensor_scale(MODE)) {
-    s_t = tensor_scale<kMxThreads>(p, red);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
-  }
-  mx_build_frags<0>(p.sg, fr);
-  __syncthreads();
   const uint32_t lane = threadIdx.x & 63u, j = lane & 31u, h = lane >> 5;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t G = p.K16 >> 3;  // groups per row
@@ -913,7 +956,20 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_rows_mx(QuantParams p) {
   uint32_t gbq = 0u;
   bool actq = false;
   uint32_t T = __builtin_amdgcn_readfirstlane(blockIdx.x * (kMxThreads / kWave) + (threadIdx.x >> 6));
-  if (T < ntiles) load_tile(T);
+  // Without a tensor-scale reduction (which uses the stage), the first
+  // tile's loads are in flight while the fragments are built.
+  float s_t = 1.0f;
+  if constexpr (takes_tensor_scale(MODE)) {
+    s_t = tensor_scale<kMxThreads>(p, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  } else {
+    if (T < ntiles) load_tile(T);
+  }
+  mx_build_frags<0>(p.sg, fr);
+  __syncthreads();
+  if constexpr (takes_tensor_scale(MODE)) {
+    if (T < ntiles) load_tile(T);
+  }
   for (; T < ntiles; T += waves) {
     // the staged tile (direct-to-LDS loads count in vmcnt only; earlier
     // stores were issued before these loads)
@@ -980,13 +1036,6 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_cols_mx(QuantParams p) {
   __shared__ uint4 stage[2048];  // 256 rows x 8 chunks
   // (the reductions before and after the loop use the stage's first bytes)
   float *const red = reinterpret_cast<float *>(&stage[0]);
-  float s_t = 1.0f;
-  if constexpr (takes_tensor_scale(MODE)) {
-    s_t = tensor_scale<kMxThreads>(p, red);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
-  }
-  mx_build_frags<1>(p.sg, fr);
-  __syncthreads();
   const uint32_t lane = threadIdx.x & 63u, j = lane & 31u, h = lane >> 5;
   const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ngroups = p.rows >> 7;
@@ -1029,7 +1078,20 @@ __global__ __launch_bounds__(kMxThreads) void k_quant_cols_mx(QuantParams p) {
   uint32_t gbq = 0u;
   bool colq = false, grp1q = false;
   uint32_t T = first + (blockIdx.x >> 3);
-  if (T < last) load_tile(T);
+  // Without a tensor-scale reduction (which uses the stage), the first
+  // tile's loads are in flight while the fragments are built.
+  float s_t = 1.0f;
+  if constexpr (takes_tensor_scale(MODE)) {
+    s_t = tensor_scale<kMxThreads>(p, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.ts_out = s_t;
+  } else {
+    if (T < last) load_tile(T);
+  }
+  mx_build_frags<1>(p.sg, fr);
+  __syncthreads();
+  if constexpr (takes_tensor_scale(MODE)) {
+    if (T < last) load_tile(T);
+  }
   for (; T < last; T += step) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the tile
     __builtin_amdgcn_s_barrier();        // ... and every wave's
