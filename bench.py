@@ -315,10 +315,12 @@ def main():
     ]
     outs = {n: qt(r, k) for n, _, _, _, _, r, k in plan}
     wss = {n: ws_for(x.shape[0], x.shape[1], rnd, ax) for n, x, rnd, ax, _, _, _ in plan}
-    # X and W are quantized column-wise (for the gradients) before their
+    # X and W are quantized column-wise (for the gradients) right before their
     # row-wise RTN (for Y): each column-wise MS-EDEN pass also writes max|x|,
     # the row-wise RTN's tensor scale takes it, and X and W are read once
-    # less than with a separate maximum pass.
+    # less than with a separate maximum pass.  The two passes over a tensor
+    # run back to back, so the row pass finds part of the tensor still in the
+    # 256 MB memory-side cache (all of W's 90 MB, part of X's 268 MB).
     amax = {"X": torch.zeros(1, dtype=torch.float32, device=dev),
             "W": torch.zeros(1, dtype=torch.float32, device=dev)}
     handoff = {"qXc": {"amax_out": amax["X"]}, "qWc": {"amax_out": amax["W"]},
@@ -357,7 +359,7 @@ def main():
             nv.gemm_nvfp4(outs[qa], outs[qb], out=out)
             marks.append(("g", name, a, ev() if timed else None))
 
-        q(("qXc", "qWc", "qX", "qW"))     # column-wise first: they hand max|x| on
+        q(("qXc", "qX", "qWc", "qW"))     # per tensor, column-wise first: it hands max|x| on
         g("Y", "qX", "qW", Y)
         q(("qdYr",))
         g("dX", "qdYr", "qWc", dX)
@@ -438,7 +440,7 @@ def main():
         "config": {"workload": "mlp_up_projection_training_step", "X": [T, D], "W": [O, D],
                    "dY": [T, O], "input_dtype": "bf16", "rotation": 128,
                    "quantizations": "RTN(X,W) fwd; RHT+MS-EDEN(dY row+col, W col, X col) bwd; "
-                                    "X, W col first, handing max|x| to their row RTN",
+                                    "X col then X row, W col then W row: each col pass hands max|x| to its row RTN",
                    "gemms": "Y=XW^T (bf16), dX=dY W (bf16), dW=dY^T X (fp32)"},
         "hbm_frac": round(q_gbs / HBM_PEAK_GBS, 3),
         "gemm": {"value": round(g_tflops, 1), "unit": "TFLOP/s",
