@@ -1535,6 +1535,20 @@ __device__ __forceinline__ uint32_t eden_scale_byte_fix(float t, const Divisor &
 template <int IF4>
 __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
   __shared__ float red[kThreads / kWave];
+  // Whole calls (8 blocks each).  This thread's first call's targets do not
+  // depend on the tensor scale: their loads are in flight during its
+  // reduction (clamped to the last whole call, so they are unconditional
+  // within a grid that has one).
+  const uint32_t nfull = p.nblocks / 8u;
+  const uint32_t stride = gridDim.x * kThreads;
+  const float4 *tb = reinterpret_cast<const float4 *>(p.tb);
+  uint32_t c = blockIdx.x * kThreads + threadIdx.x;
+  float4 a0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), a1 = a0;
+  if (nfull != 0u) {
+    const uint32_t c0 = c < nfull ? c : nfull - 1u;
+    a0 = tb[2 * (size_t)c0];
+    a1 = tb[2 * (size_t)c0 + 1];
+  }
   float s_t;
   if (p.ts_in) {
     s_t = *p.ts_in;
@@ -1548,10 +1562,8 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     if (threadIdx.x == 0) *p.amax_out = m;
   }
   const Divisor dst = make_divisor(s_t);
-  // Whole calls (8 blocks each): the next call's targets are loaded while
-  // this one is coded (clamped to the last call, so the load is unconditional).
-  const uint32_t nfull = p.nblocks / 8u;
-  const uint32_t stride = gridDim.x * kThreads;
+  // The next call's targets are loaded while this one is coded (clamped to
+  // the last call, so the load is unconditional).
   auto code8 = [&](uint32_t c, const float4 &t0, const float4 &t1) {
     const Philox4 u = uniforms8(p.key, (uint64_t)c, 1u);
     const float t[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
@@ -1564,10 +1576,7 @@ __global__ __launch_bounds__(kThreads) void k_eden_scales(QuantParams p) {
     }
     *reinterpret_cast<uint2 *>(p.scales + (size_t)c * 8) = make_uint2(lo, hi);
   };
-  uint32_t c = blockIdx.x * kThreads + threadIdx.x;
   if (c < nfull) {
-    const float4 *tb = reinterpret_cast<const float4 *>(p.tb);
-    float4 a0 = tb[2 * (size_t)c], a1 = tb[2 * (size_t)c + 1];
     for (; c < nfull; c += stride) {
       const uint32_t cn = c + stride < nfull ? c + stride : nfull - 1;
       const float4 n0 = tb[2 * (size_t)cn], n1 = tb[2 * (size_t)cn + 1];
