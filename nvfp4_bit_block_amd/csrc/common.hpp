@@ -375,29 +375,27 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, _Float16 s) {
 
 // IF4 operands: a block whose scale byte has bit 7 set holds sign-magnitude
 // integers 0..7 instead of E2M1 codes.  Every magnitude of either kind is an
-// fp16 value with a zero low byte, so one byte permute per pair of codes
-// looks up the high bytes in a 16-byte table chosen by the block's flag:
+// fp16 value with a zero low byte, and its high byte (below 0x80) comes from
+// a 16-byte table chosen by the block's flag:
 //   E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6} -> 00 38 3C 3E 40 42 44 46
 //   INT  {0, 1, 2, 3, 4, 5, 6, 7}    -> 00 3C 40 42 44 45 46 47
 constexpr uint32_t kLutFpLo = 0x3E3C3800u, kLutFpHi = 0x46444240u;
 constexpr uint32_t kLutIntLo = 0x42403C00u, kLutIntHi = 0x47464544u;
 
 // 8 codes of one block (element 2i in the low nibble of byte i), decoded
-// through the table {lut_hi:lut_lo}, times one fp16 scale.
+// through the table {lut_hi:lut_lo}, times one fp16 scale.  One byte
+// permute looks up the high bytes of the four even elements (magnitudes
+// in the low nibbles) and one those of the four odd ones; each code's sign
+// bit (bit 3 of its nibble) is then set as bit 7 of its byte, the fp16 sign;
+// four more permutes spread the bytes into fp16 pairs [0, even, 0, odd].
 __device__ __forceinline__ half8_t dequant8_lut(uint32_t w, _Float16 s, uint32_t lut_lo, uint32_t lut_hi) {
   const half2_t s2 = {s, s};
-  const uint32_t lo_n = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-  const uint32_t hi_n = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+  const uint32_t ev = __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u) | ((w << 4) & 0x80808080u);
+  const uint32_t od = __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
   half8_t out;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    // bytes [0, code 2k, 0, code 2k+1]
-    const uint32_t h = __builtin_amdgcn_perm(hi_n, lo_n, 0x000C000Cu | ((4u + k) << 24) | ((uint32_t)k << 8));
-    // selector [zero, magnitude, zero, magnitude] -> fp16 magnitudes
-    const uint32_t sel = (h & 0x07000700u) | 0x000C000Cu;
-    const uint32_t mag = __builtin_amdgcn_perm(lut_hi, lut_lo, sel);
-    // sign bits 11 and 27 of h move to the fp16 sign bits 15 and 31
-    const uint32_t v = ((h << 4) & 0x80008000u) | mag;
+    const uint32_t v = __builtin_amdgcn_perm(od, ev, 0x000C000Cu | ((4u + k) << 24) | ((uint32_t)k << 8));
     const half2_t p = __builtin_bit_cast(half2_t, v) * s2;
     out[2 * k] = p[0];
     out[2 * k + 1] = p[1];
