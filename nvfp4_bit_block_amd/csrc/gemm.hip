@@ -55,6 +55,7 @@ namespace nv4 {
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kTile = 256, kWaveCols = 64, kChunk = 64, kSteps = 4, kGroupM = 4, kXcds = 8;
 
@@ -241,6 +242,10 @@ __device__ __forceinline__ uint32_t rtn_block16(const float z[16], float s_t, ui
 // bytes and eight (bf16) or sixteen (fp32) lanes cover a whole row of the
 // wave tile.  The 16-byte column chunks of a row are XOR-swizzled by the
 // row so that both the writes and the reads spread over all LDS banks.
+// The bf16 and fp32 rows are written with non-temporal stores: an output of
+// this size is not read again while it could still be in the caches, and
+// dirty lines left in L2 and the memory-side cache would be written back
+// while the next kernel runs, at that kernel's expense.
 template <int OUT>
 __device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][2], const GemmParams &p, uint32_t m0,
                                            uint32_t n0, uint32_t w, float &qmax) {
@@ -288,7 +293,7 @@ __device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][
       if (row >= p.M || col >= p.N) continue;
       uint16_t *dst = static_cast<uint16_t *>(p.c) + (size_t)row * p.ldc + col;
       if (vec && col + 8 <= p.N) {
-        *reinterpret_cast<uint4 *>(dst) = v;
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(dst));
       } else {
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -343,7 +348,7 @@ __device__ __forceinline__ void store_tile(Stage &st, const float16_t (&acc)[2][
         if (row >= p.M || col >= p.N) continue;
         float *dst = static_cast<float *>(p.c) + (size_t)row * p.ldc + col;
         if (vec && col + 4 <= p.N) {
-          *reinterpret_cast<float4 *>(dst) = v;
+          __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t *>(dst));
         } else {
           const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
