@@ -283,7 +283,11 @@ __device__ __forceinline__ Philox4 uniforms8(const RngKey &k, uint64_t call, uin
 }
 
 __device__ __forceinline__ uint32_t uniform_at(const Philox4 &p, int j) {
-  return (p.w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+  // (word chosen by selects, not by indexing: an index the compiler cannot
+  // resolve would put the four words in scratch memory)
+  const int k = j >> 1;
+  const uint32_t w = k == 0 ? p.w[0] : k == 1 ? p.w[1] : k == 2 ? p.w[2] : p.w[3];
+  return (w >> (16 * (j & 1))) & 0xFFFFu;
 }
 
 // ---------------------------------------------------------------- division
