@@ -1238,9 +1238,12 @@ __device__ __forceinline__ void col_tile(const QuantParams &p, uint32_t tt, uint
 #pragma unroll
   for (uint32_t j = 0; j < C::kColCols; ++j) {
     const int wi = IN_BF16 ? (int)(j >> 1) : (int)j;
+    // (words taken by selects: when the compiler leaves this loop rolled, as
+    // for the larger block codes, an index would move the tile to scratch)
     uint32_t cw[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cw[r] = w[r][wi];
+    for (int r = 0; r < 16; ++r)
+      cw[r] = wi == 0 ? w[r][0] : wi == 1 ? w[r][1] : wi == 2 ? w[r][2] : w[r][3];
     float z[16];
     auto unpack = [&]() {
 #pragma unroll
