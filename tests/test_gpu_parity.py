@@ -349,6 +349,33 @@ def test_tensor_scale_in(nv):
         assert_bit_exact(q, ref, f"ts_in rounding {rnd}")
 
 
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("group", [128, 16])
+def test_mseden_given_scale_rotation(nv, axis, group):
+    """MS-EDEN with a given tensor scale and the rotation: codes and scales in
+    one pass, each block's scale rounded with the uniform at its position in
+    its Philox word (bf16: the matrix-core kernels; fp32: the butterflies).
+    Several tiles, a ragged tail, every position 0..7 of the uniforms."""
+    import torch
+    rng = np.random.default_rng(47)
+    signs = synth.signs_from_rng(rng)
+    w = oracle.signs_words(signs)
+    shapes = [(200, 1024), (33, 384)] if axis == 0 else [(1024, 200), (384, 33)]
+    for dtype in ("bf16", "fp32"):
+        for i, (r, c) in enumerate(shapes):
+            x = synth.gradient(r, c, seed=900 + i)[0]
+            amax = float(np.max(np.abs(x)))
+            ts = np.float32(amax / 2688.0)
+            g = q_to_host(nv.quantize_nvfp4(to_device(x, dtype), rounding=oracle.MSEDEN, axis=axis,
+                                            rht_signs=signs, seed=13, stream_id=3, eden_group=group,
+                                            tensor_scale_in=torch.tensor([ts], device="cuda:0")))
+            ref = oracle.quantize(x, rounding=oracle.MSEDEN, axis=axis, rht_on=True, signs_w=w, seed=13, stream=3,
+                                  eden_group=group, ts_in=float(ts))
+            assert g["ts"] == float(ts)
+            assert_rotated_close(g, ref, what=f"mseden given scale {dtype} axis{axis} group{group} {r}x{c}")
+            assert len(np.unique(ref["scales"])) > 8
+
+
 def upload(nv, ref, fmt):
     """A QTensor on the device holding the oracle's packed output."""
     import torch
