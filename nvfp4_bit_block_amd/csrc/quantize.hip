@@ -311,25 +311,34 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       const uint32_t ei = e4m3_rne_sat(div_rn(div_by<7>(a), s_t));
       const float Si = e4m3_value(ei) * s_t;
       const float ri = ei ? rcp_rn(Si) : 0.0f;
-      float sqf[16], sqi[16], y[16], vf[16];
-      uint32_t flo, fhi, ilo = 0, ihi = 0;
+      float sqf[16], sqi[16], y[16], vf[16], vi[16];
+      uint32_t flo, fhi;
 #pragma unroll
       for (int i = 0; i < 16; ++i) y[i] = z[i] * rf;
       e2m1x16_rne(y, flo, fhi);
       e2m1x16_value(flo, fhi, vf);  // signed grid values
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t sn = sign_nib(z[i]);
         const float df = z[i] - vf[i] * Sf;
         sqf[i] = df * df;
-        uint32_t mi = 0;
-        if (ei) mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
-        const float vi = (float)mi;
-        const float di = z[i] - (sn ? -vi : vi) * Si;
+        // the integer magnitude (0 when ei = 0: ri = 0); the error of the
+        // signed value sign(z) * vi * Si is the negation of |z| - vi * Si
+        // under the same rounding, so its square is the same
+        vi[i] = rintf(fminf(fabsf(z[i] * ri), 7.0f));
+        const float di = fabsf(z[i]) - vi[i] * Si;
         sqi[i] = di * di;
-        if (i < 8) ilo |= (sn | mi) << (4 * i);
-        else ihi |= (sn | mi) << (4 * (i - 8));
       }
+      // the INT codes: magnitudes two per byte (vi[2j] + 16 vi[2j+1] is an
+      // exact integer below 128), signs from the E2M1 codes, which carry
+      // z's sign bit whatever they round to
+      uint32_t ilo = 0, ihi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ilo = __builtin_amdgcn_cvt_pk_u8_f32(vi[2 * j] + 16.0f * vi[2 * j + 1], j, ilo);
+        ihi = __builtin_amdgcn_cvt_pk_u8_f32(vi[8 + 2 * j] + 16.0f * vi[9 + 2 * j], j, ihi);
+      }
+      ilo |= flo & 0x88888888u;
+      ihi |= fhi & 0x88888888u;
       const bool use_int = tree16(sqi) < tree16(sqf);
       out.codes(use_int ? ilo : flo, use_int ? ihi : fhi);
       out.scale(use_int ? (ei | 0x80u) : ef);
