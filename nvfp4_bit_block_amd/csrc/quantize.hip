@@ -195,27 +195,30 @@ __device__ __forceinline__ EdenBlock eden_codes(const float z[16], float a) {
   if constexpr (IF4) {
     const float si = div_by<7>(a);
     const float ri = (a > 0.0f) ? rcp_rn(si) : 0.0f;
-    float sqf[16], sqi[16], gi[16];
-    uint32_t ilo = 0, ihi = 0;
+    // (the INT branch as in IF4 RTN: magnitudes as floats, the error from
+    // |z|, codes packed per byte with the E2M1 codes' sign bits)
+    float sqf[16], sqi[16], vi[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float df = z[i] - g[i] * b.s_b;
       sqf[i] = df * df;
-      const uint32_t sn = sign_nib(z[i]);
-      const uint32_t mi = (uint32_t)rintf(fminf(fabsf(z[i] * ri), 7.0f));
-      gi[i] = sn ? -(float)mi : (float)mi;
-      const float di = z[i] - gi[i] * si;
+      vi[i] = rintf(fminf(fabsf(z[i] * ri), 7.0f));
+      const float di = fabsf(z[i]) - vi[i] * si;
       sqi[i] = di * di;
-      if (i < 8) ilo |= (sn | mi) << (4 * i);
-      else ihi |= (sn | mi) << (4 * (i - 8));
     }
     b.use_int = tree16(sqi) < tree16(sqf);
     if (b.use_int) {
-      b.lo = ilo;
-      b.hi = ihi;
+      uint32_t ilo = 0, ihi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ilo = __builtin_amdgcn_cvt_pk_u8_f32(vi[2 * j] + 16.0f * vi[2 * j + 1], j, ilo);
+        ihi = __builtin_amdgcn_cvt_pk_u8_f32(vi[8 + 2 * j] + 16.0f * vi[9 + 2 * j], j, ihi);
+      }
+      b.lo = ilo | (b.lo & 0x88888888u);
+      b.hi = ihi | (b.hi & 0x88888888u);
       b.s_b = si;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) g[i] = gi[i];
+      for (int i = 0; i < 16; ++i) g[i] = copysignf(vi[i], z[i]);  // signed integer values
     }
   }
 #pragma unroll
