@@ -430,6 +430,17 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
         const int e = e0 + (t + 1) / 2 * ((t & 1) ? -1 : 1);
         if (t > 0 && (e < 1 || e > 126)) continue;
         const float S = e4m3_value((uint32_t)e) * s_t;
+        if (t > 0) {
+          // A scale with 6 S < a codes the largest element as 6: that
+          // element's own term, (a - 6 S)^2 rounded as in the sum below, is
+          // a lower bound of the rounded sum (every term is >= 0).  A trial
+          // whose bound reaches the best sum cannot be strictly smaller.
+          const float p6 = 6.0f * S;
+          if (p6 < a) {
+            const float d = a - p6;
+            if (d * d >= best) continue;
+          }
+        }
         const float r = e ? rcp_rn(S) : 0.0f;
         float y[16], v[16], sq[16];
         uint32_t lo, hi;
