@@ -931,9 +931,11 @@ __device__ __forceinline__ void mx_store_cols(const QuadOut &q, uint32_t gb0, ui
 // (SR is held to three waves per SIMD, 168 VGPRs: it would take 176, and
 // the few values the compiler then keeps in scratch cost less than the
 // third wave gains -- the whole SR call on a 32768x11008 gradient is 4 %
-// faster along rows, 7 % along columns)
+// faster along rows, 7 % along columns.  MS-EDEN with max|x| out would take
+// 170 and fits in 168 without spilling.)
 template <int MODE, int RAW = 0>
-__global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(MODE == kSr ? 3 : 1)))
+__global__ __launch_bounds__(kMxThreads)
+__attribute__((amdgpu_waves_per_eu(MODE == kSr || (MODE == kEden && RAW) ? 3 : 1)))
 void k_quant_rows_mx(QuantParams p) {
   typedef __attribute__((address_space(3))) void lds_void;
   __shared__ RotFrags fr;
