@@ -359,15 +359,15 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
       float yf[16], yi[16], df[16], di[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        yf[i] = ef ? fminf(fabsf(z[i] * rf), 6.0f) : 0.0f;
-        yi[i] = ei ? fminf(fabsf(z[i] * ri), 7.0f) : 0.0f;
+        // (a zero scale byte has a zero reciprocal: y = 0 without a select)
+        yf[i] = fminf(fabsf(z[i] * rf), 6.0f);
+        yi[i] = fminf(fabsf(z[i] * ri), 7.0f);
         df[i] = e2m1_sr_err(yf[i]);
         di[i] = int4_sr_err(yi[i]);
       }
       const bool use_int = (Si * Si) * tree16(di) < (Sf * Sf) * tree16(df);
       const Philox4 u0 = uniforms8(p.key, (uint64_t)gb * 2u, 0u);
       const Philox4 u1 = uniforms8(p.key, (uint64_t)gb * 2u + 1u, 0u);
-      const bool coded = use_int ? (ei != 0u) : (ef != 0u);
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -381,7 +381,8 @@ __device__ __forceinline__ void quant_block(float z[16], uint32_t gb, const Sink
         const float f = floorf(ys);
         const uint32_t up = ((float)u < (ys - f) * 65536.0f) ? 1u : 0u;
         const uint32_t mag0 = (uint32_t)f + up + (use_int ? 0u : (uint32_t)(2 * E));
-        const uint32_t mag = coded ? (y >= top ? 7u : mag0) : 0u;
+        // (y = 0 where the kept scale byte is 0, and then mag0 = 0 too)
+        const uint32_t mag = y >= top ? 7u : mag0;
         const uint32_t nib = sign_nib(z[i]) | mag;
         if (i < 8) lo |= nib << (4 * i);
         else hi |= nib << (4 * (i - 8));
